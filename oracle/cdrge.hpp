@@ -1,0 +1,186 @@
+// CPU oracle — test infrastructure only. Nothing in the product path may include or link this.
+//
+// Central-difference random-vector gradient estimation (CD-RGE), one update step at a time.
+//
+// The method (pith.science review of arXiv 2505.17852, "What carries the argument"; alex-wiki
+// source note, "Method"):
+//   g_hat  = (1/K) * sum_i [ L(theta + eps p_i) - L(theta - eps p_i) ] / (2 eps) * p_i
+//   theta' = theta - eta * g_hat = theta - eta / (2 K eps) * sum_i d_i p_i,
+//   d_i    = L(theta + eps p_i) - L(theta - eps p_i),
+// with Rademacher p_i regenerated from per-probe seeds (philox.hpp) and, in the paper's runs,
+// eta = eps (the review's version of the update, 1/(2 n_pert) * sum d_i p_i, is the eta = eps case).
+//
+// Readings taken where the pages are silent (each one is listed in the design notes):
+//   * losses[2i] = L(theta + eps p_i), losses[2i+1] = L(theta - eps p_i).
+//   * The perturbed model never overwrites theta: the "perturb in place, forward, restore" of the
+//     alex-wiki note is taken to restore exactly, so a perturbed copy is built per forward.
+//   * Perturbed weight in the model's storage precision: fp32 storage uses the float sum
+//     float(w) + float(+-eps); bf16 storage rounds that float sum once more to bf16. Exact
+//     storage (double, used only by the estimator checks) adds in double.
+//   * coef = eta / (2 K eps) is evaluated in double and rounded once to float, d_i is the float
+//     difference of the float losses, the sum over probes and the step are evaluated in double
+//     and the result is rounded once to the storage precision.
+//   * Any non-finite loss leaves theta unchanged and reports an error.
+#pragma once
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "bf16.hpp"
+#include "lstm.hpp"
+#include "philox.hpp"
+
+namespace oracle {
+
+enum class Storage { F32 = 0, BF16 = 1, F64 = 2 };
+
+// Reads a stored parameter as a double.
+inline double load_param(const void* theta, Storage s, int64_t j) {
+  switch (s) {
+    case Storage::F32: return static_cast<const float*>(theta)[j];
+    case Storage::BF16: return bf16_to_f32(static_cast<const uint16_t*>(theta)[j]);
+    default: return static_cast<const double*>(theta)[j];
+  }
+}
+
+// Writes x to a stored parameter, rounding once to the storage precision.
+inline void store_param(void* theta, Storage s, int64_t j, double x) {
+  switch (s) {
+    case Storage::F32: static_cast<float*>(theta)[j] = static_cast<float>(x); break;
+    case Storage::BF16: static_cast<uint16_t*>(theta)[j] = f64_to_bf16(x); break;
+    default: static_cast<double*>(theta)[j] = x; break;
+  }
+}
+
+// The perturbed weight w + sigma * eps * p in the storage precision (see the header comment).
+inline double perturbed_param(double w, Storage s, int signed_unit, float eps) {
+  switch (s) {
+    case Storage::F32: {
+      const float sum = static_cast<float>(w) + static_cast<float>(signed_unit) * eps;
+      return sum;
+    }
+    case Storage::BF16: {
+      const float sum = static_cast<float>(w) + static_cast<float>(signed_unit) * eps;
+      return bf16_to_f32(f32_to_bf16(sum));
+    }
+    default: return w + static_cast<double>(signed_unit) * static_cast<double>(eps);
+  }
+}
+
+// Locates flat element j in the layout: tensor id, row and column.
+struct ElementIndex {
+  uint32_t tensor, row, col;
+};
+
+class LayoutIndexer {
+ public:
+  explicit LayoutIndexer(const std::vector<TensorInfo>& lay) : lay_(lay) {}
+  ElementIndex at(int64_t j) {
+    while (!(j >= lay_[cur_].offset && j < lay_[cur_].offset + lay_[cur_].rows * lay_[cur_].cols)) {
+      cur_ = (j < lay_[cur_].offset) ? cur_ - 1 : cur_ + 1;
+    }
+    const TensorInfo& t = lay_[cur_];
+    const int64_t local = j - t.offset;
+    return ElementIndex{t.id, static_cast<uint32_t>(local / t.cols), static_cast<uint32_t>(local % t.cols)};
+  }
+
+ private:
+  const std::vector<TensorInfo>& lay_;
+  size_t cur_ = 0;
+};
+
+// The full Rademacher probe vector for one seed, as +-1 per flat element.
+inline std::vector<int8_t> probe_vector(const std::vector<TensorInfo>& lay, uint64_t seed) {
+  const int64_t d = layout_size(lay);
+  std::vector<int8_t> p(d);
+  for (const TensorInfo& t : lay)
+    for (int64_t r = 0; r < t.rows; ++r)
+      for (int64_t c = 0; c < t.cols; ++c)
+        p[t.offset + r * t.cols + c] = static_cast<int8_t>(
+            probe_sign(seed, t.id, static_cast<uint32_t>(r), static_cast<uint32_t>(c)));
+  return p;
+}
+
+// Perturbed copy theta + sigma * eps * p (storage rounding applied), as element type P.
+template <class P>
+void perturbed_copy(const std::vector<TensorInfo>& lay, const void* theta, Storage s, uint64_t seed,
+                    int sigma, float eps, std::vector<P>& out) {
+  const int64_t d = layout_size(lay);
+  out.resize(d);
+  for (const TensorInfo& t : lay)
+    for (int64_t r = 0; r < t.rows; ++r)
+      for (int64_t c = 0; c < t.cols; ++c) {
+        const int64_t j = t.offset + r * t.cols + c;
+        const int p = probe_sign(seed, t.id, static_cast<uint32_t>(r), static_cast<uint32_t>(c));
+        out[j] = static_cast<P>(perturbed_param(load_param(theta, s, j), s, sigma * p, eps));
+      }
+}
+
+// Losses of probes `probe_ids` for a generic loss functor: loss(perturbed weights) -> double.
+// out[2k] = L(theta + eps p_{probe_ids[k]}), out[2k+1] = L(theta - eps p_{probe_ids[k]}).
+template <class P, class LossFn>
+void probe_losses_generic(const std::vector<TensorInfo>& lay, const void* theta, Storage s,
+                          uint64_t base_seed, uint64_t step, const int* probe_ids, int n_ids,
+                          float eps, LossFn loss, double* out) {
+  std::vector<P> w;
+  for (int k = 0; k < n_ids; ++k) {
+    const uint64_t seed = probe_seed(base_seed, step, static_cast<uint32_t>(probe_ids[k]));
+    for (int side = 0; side < 2; ++side) {
+      const int sigma = (side == 0) ? +1 : -1;
+      perturbed_copy(lay, theta, s, seed, sigma, eps, w);
+      out[2 * k + side] = loss(w);
+    }
+  }
+}
+
+// The update coefficient eta / (2 K eps), rounded once to float.
+inline float update_coef(int K, float eps, float lr) {
+  return static_cast<float>(static_cast<double>(lr) / (2.0 * K * static_cast<double>(eps)));
+}
+
+// theta <- theta - coef * sum_i d_i p_i over the elements listed in `elems` (all when null).
+// Returns 0, or 1 when a loss is not finite (theta then untouched).
+// LossT is float for the model path (d_i is then a float difference, as the losses are floats)
+// and double for the estimator checks on exact storage.
+template <class LossT>
+int cdrge_update(const std::vector<TensorInfo>& lay, void* theta, Storage s, uint64_t base_seed,
+                 uint64_t step, int K, const LossT* losses, float eps, float lr,
+                 const int64_t* elems, int64_t n_elems) {
+  for (int i = 0; i < 2 * K; ++i)
+    if (!std::isfinite(losses[i])) return 1;
+  std::vector<LossT> dif(K);
+  std::vector<uint64_t> seeds(K);
+  for (int i = 0; i < K; ++i) {
+    dif[i] = losses[2 * i] - losses[2 * i + 1];
+    seeds[i] = probe_seed(base_seed, step, static_cast<uint32_t>(i));
+  }
+  const double coef = update_coef(K, eps, lr);
+  LayoutIndexer index(lay);
+  const int64_t n = elems ? n_elems : layout_size(lay);
+  for (int64_t q = 0; q < n; ++q) {
+    const int64_t j = elems ? elems[q] : q;
+    const ElementIndex e = index.at(j);
+    double acc = 0.0;
+    for (int i = 0; i < K; ++i) {
+      const int p = probe_sign(seeds[i], e.tensor, e.row, e.col);
+      acc += (p > 0) ? static_cast<double>(dif[i]) : -static_cast<double>(dif[i]);
+    }
+    store_param(theta, s, j, load_param(theta, s, j) - coef * acc);
+  }
+  return 0;
+}
+
+// Mean LSTM loss over all B sequences (in double), rounded to float as the loss value.
+template <class P>
+double lstm_mean_loss(const ModelShape& m, const std::vector<P>& w, const int32_t* tokens,
+                      bool round_act_bf16) {
+  std::vector<int> ids(m.B);
+  for (int b = 0; b < m.B; ++b) ids[b] = b;
+  std::vector<double> seq(m.B);
+  lstm_sequence_losses<double, P>(m, w.data(), tokens, ids.data(), m.B, round_act_bf16, seq.data());
+  double total = 0.0;
+  for (int b = 0; b < m.B; ++b) total += seq[b];
+  return total / (static_cast<double>(m.B) * m.T);
+}
+
+}  // namespace oracle

@@ -1,0 +1,87 @@
+"""Pins for the oracle's LSTM language-model loss against torch's own modules.
+
+torch.nn.LSTM (gate order i, f, g, o), nn.Embedding-style lookup, nn.functional.linear and
+nn.functional.cross_entropy compute, in float64 on the CPU, the model the oracle defines (one bias
+per layer: torch's bias_hh is set to zero). A dropped term, a transposed weight, a wrong gate order
+or a shifted target index in the oracle changes these losses far beyond the tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import OracleConfig
+
+SHAPES = [
+    dict(n_layers=1, vocab=16, embed=16, hidden=32, batch=4, seq_len=10),   # the tiny workload
+    dict(n_layers=2, vocab=7, embed=8, hidden=12, batch=3, seq_len=5),
+    dict(n_layers=3, vocab=50, embed=6, hidden=5, batch=2, seq_len=4),
+]
+
+
+def _cfg(shape, storage="f64"):
+    return OracleConfig(n_probes=1, storage=storage, eps=1e-3, lr=1e-3, base_seed=1, **shape)
+
+
+def torch_seq_losses(oracle, cfg, theta64, tokens):
+    lay = {tid: (off, rows, cols) for tid, off, rows, cols in oracle.layout(cfg)}
+
+    def tensor(tid):
+        off, rows, cols = lay[tid]
+        return torch.from_numpy(theta64[off:off + rows * cols].reshape(rows, cols).copy())
+
+    L, H = cfg.n_layers, cfg.hidden
+    lstm = torch.nn.LSTM(cfg.embed, H, num_layers=L, batch_first=True, dtype=torch.float64)
+    with torch.no_grad():
+        for l in range(L):
+            getattr(lstm, f"weight_ih_l{l}").copy_(tensor(1 + 3 * l))
+            getattr(lstm, f"weight_hh_l{l}").copy_(tensor(2 + 3 * l))
+            getattr(lstm, f"bias_ih_l{l}").copy_(tensor(3 + 3 * l).reshape(-1))
+            getattr(lstm, f"bias_hh_l{l}").zero_()
+        emb = tensor(0)
+        tok = torch.from_numpy(tokens.astype(np.int64))
+        x = emb[tok[:, :-1]]
+        out, _ = lstm(x)
+        logits = torch.nn.functional.linear(out, tensor(1 + 3 * L), tensor(2 + 3 * L).reshape(-1))
+        ce = torch.nn.functional.cross_entropy(logits.reshape(-1, cfg.vocab), tok[:, 1:].reshape(-1),
+                                               reduction="none")
+        return ce.reshape(cfg.batch, cfg.seq_len).sum(dim=1).numpy()
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_forward_matches_torch_lstm(oracle, shape):
+    cfg = _cfg(shape)
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(21)
+    theta = rng.uniform(-0.6, 0.6, d)
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    got = oracle.seq_losses(cfg, theta, tokens)
+    ref = torch_seq_losses(oracle, cfg, theta, tokens)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=0)
+
+
+def test_forward_fp32_storage_reads_weights_exactly(oracle):
+    cfg = _cfg(SHAPES[0], storage="f32")
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(22)
+    theta32 = rng.uniform(-0.2, 0.2, d).astype(np.float32)
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    got = oracle.seq_losses(cfg, theta32, tokens)
+    ref = torch_seq_losses(oracle, cfg, theta32.astype(np.float64), tokens)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=0)
+
+
+def test_param_count_and_layout(oracle):
+    # single-bias layout: V*E + sum_l (4H*in_l + 4H*H + 4H) + V*H + V
+    for shape in SHAPES:
+        cfg = _cfg(shape)
+        V, E, H, L = cfg.vocab, cfg.embed, cfg.hidden, cfg.n_layers
+        expect = V * E + sum(4 * H * (E if l == 0 else H) + 4 * H * H + 4 * H for l in range(L)) + V * H + V
+        assert oracle.param_count(cfg) == expect
+        lay = oracle.layout(cfg)
+        assert [t[0] for t in lay] == list(range(3 * L + 3))
+        assert all(lay[i + 1][1] == lay[i][1] + lay[i][2] * lay[i][3] for i in range(len(lay) - 1))
+    big = [(1, 64, 256, 32, 338_976), (2, 128, 1024, 50, 13_173_042), (2, 4096, 4096, 50, 268_877_874),
+           (4, 5888, 5888, 50, 1_110_076_466), (1, 16, 32, 16, 7_056)]
+    for L, E, H, V, d in big:
+        cfg = OracleConfig(L, V, E, H, 1, 1, 1, "f32", 1e-3, 1e-3, 1)
+        assert oracle.param_count(cfg) == d

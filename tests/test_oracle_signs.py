@@ -1,0 +1,76 @@
+"""Pin (d): the probe signs are balanced Rademacher entries with E[p p^T] = I.
+
+The review of arXiv 2505.17852 (pith.science, "assumptions": probes zero-mean and isotropic,
+E[p]=0 and E[pp^T]=I) and its Rademacher choice ("What carries the argument") fix what the sign
+stream must satisfy. Checked statistically over about 1e7 signs with 5-sigma bounds, including the
+coordinate pairs a faulty bit mapping would correlate (neighbouring columns, the two half-words
+of one Philox word, neighbouring rows, the four words of one call).
+"""
+import numpy as np
+
+from oracle import OracleConfig
+
+
+def _probes(oracle, k=32):
+    cfg = OracleConfig(1, 32, 64, 256, 1, 100, k, "f32", 1e-3, 1e-3, 3002)
+    P = np.stack([oracle.probe_vector(cfg, oracle.probe_seed(cfg.base_seed, 0, i)) for i in range(k)])
+    return cfg, P.astype(np.int8)
+
+
+def test_signs_balanced_and_isotropic(oracle):
+    cfg, P = _probes(oracle)
+    k, d = P.shape
+    n = P.size
+    assert n > 1e7
+    assert set(np.unique(P)) == {-1, 1}
+    assert abs(P.astype(np.float64).mean()) < 5 / np.sqrt(n)
+    G = (P.astype(np.float64) @ P.T.astype(np.float64)) / d
+    np.testing.assert_array_equal(np.diag(G), 1.0)
+    off = G[~np.eye(k, dtype=bool)]
+    assert np.abs(off).max() < 5 / np.sqrt(d)
+
+
+def test_each_bit_position_balanced(oracle):
+    cfg, P = _probes(oracle)
+    lay = {t[0]: t for t in oracle.layout(cfg)}
+    _, off, rows, cols = lay[2]                      # W_hh [1024][256]
+    W = P[:, off:off + rows * cols].reshape(P.shape[0], rows, cols // 128, 128).astype(np.float64)
+    per_pos = W.mean(axis=(0, 1, 2))
+    m = W.shape[0] * W.shape[1] * W.shape[2]
+    assert np.abs(per_pos).max() < 5 / np.sqrt(m)
+
+
+def test_no_correlation_between_related_coordinates(oracle):
+    cfg, P = _probes(oracle)
+    lay = {t[0]: t for t in oracle.layout(cfg)}
+    _, off, rows, cols = lay[2]
+    W = P[:, off:off + rows * cols].reshape(P.shape[0], rows, cols).astype(np.float64)
+    pairs = {
+        "next column": (W[:, :, :-1], W[:, :, 1:]),
+        "column + 16": (W[:, :, :-16], W[:, :, 16:]),
+        "column + 32": (W[:, :, :-32], W[:, :, 32:]),
+        "column + 128": (W[:, :, :-128], W[:, :, 128:]),
+        "next row": (W[:, :-1, :], W[:, 1:, :]),
+    }
+    for name, (a, b) in pairs.items():
+        prod = a * b
+        assert abs(prod.mean()) < 5 / np.sqrt(prod.size), name
+    # the same (row, column) under different tensors
+    _, off1, r1, c1 = lay[1]                          # W_ih [1024][64]
+    A = P[:, off1:off1 + r1 * c1].reshape(P.shape[0], r1, c1).astype(np.float64)
+    prod = A * W[:, :, :64]
+    assert abs(prod.mean()) < 5 / np.sqrt(prod.size)
+
+
+def test_mapping_uses_every_bit_once(oracle):
+    # Within one 128-column block every column reads a distinct (word, bit) of the Philox call.
+    seen = set()
+    for c in range(128):
+        j = c & 31
+        seen.add(((c >> 5) & 3, (j >> 1) | ((j & 1) << 4)))
+    assert len(seen) == 128
+    # and the oracle's signs follow the call: flipping to another block changes the stream
+    seed = oracle.probe_seed(1, 0, 0)
+    a = oracle.sign_block(seed, 5, 0, 64, 0, 128).astype(np.float64)
+    b = oracle.sign_block(seed, 5, 0, 64, 128, 128).astype(np.float64)
+    assert abs((a * b).mean()) < 5 / np.sqrt(a.size)
