@@ -1,0 +1,546 @@
+// Host side of the C ABI declared in include/cdrge.h: configuration checks, workspace plan,
+// kernel launch order and diagnostics. All work is enqueued on the caller's stream; the library
+// never allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "cdrge.h"
+#include "kernels_bf16.h"
+#include "kernels_common.h"
+#include "kernels_f32.h"
+#include "philox.h"
+
+using namespace cdrge;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxProbes = 1024;
+constexpr int kMaxF32Layers = 8;
+constexpr int64_t kMaxF32LdsBytes = 64 * 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Text of the last device-side failure seen by this thread (for cdrge_last_error_detail).
+thread_local char g_last_error[256] = "";
+
+cdrge_status device_error(const char* what, hipError_t e) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e),
+                static_cast<int>(e));
+  return CDRGE_ERR_DEVICE;
+}
+
+#define CDRGE_HIP(call)                                          \
+  do {                                                           \
+    const hipError_t _e = (call);                                \
+    if (_e != hipSuccess) return device_error(#call, _e);        \
+  } while (0)
+
+struct TensorDesc {
+  uint32_t id;
+  int64_t off, rows, cols;
+};
+
+struct Plan {
+  cdrge_config cfg;
+  int L, V, E, H, B, T, K, P;
+  int64_t d;
+  std::vector<TensorDesc> tensors;  // index == tensor id
+  size_t off_flags, off_seeds, off_seq, off_emb_m, off_bias_m, off_bout_m, off_h, off_c, total;
+  std::vector<size_t> off_wp, off_wm;  // per tensor id (bf16 matrices only)
+};
+
+bool basic_valid(const cdrge_config* c) {
+  if (!c || c->abi_version != CDRGE_ABI_VERSION) return false;
+  if (c->n_layers < 1 || c->vocab < 2 || c->embed < 1 || c->hidden < 1 || c->batch < 1 ||
+      c->seq_len < 1 || c->n_probes < 1 || c->probes_per_chunk < 0)
+    return false;
+  if (c->dtype != CDRGE_F32 && c->dtype != CDRGE_BF16) return false;
+  if (!std::isfinite(c->eps) || !(c->eps > 0.f) || !std::isfinite(c->lr) || c->lr < 0.f) return false;
+  return true;
+}
+
+int64_t param_count(const cdrge_config* c) {
+  const int64_t V = c->vocab, E = c->embed, H = c->hidden;
+  int64_t d = V * E + V * H + V;
+  for (int l = 0; l < c->n_layers; ++l) d += 4 * H * ((l == 0) ? E : H) + 4 * H * H + 4 * H;
+  return d;
+}
+
+cdrge_status supported(const cdrge_config* c) {
+  if (c->n_probes > kMaxProbes) return CDRGE_ERR_UNSUPPORTED;
+  const int64_t d = param_count(c);
+  if (d >= (int64_t(1) << 40)) return CDRGE_ERR_UNSUPPORTED;
+  if (int64_t(c->batch) * (c->seq_len + 1) >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+  if (c->dtype == CDRGE_F32) {
+    if (c->n_layers > kMaxF32Layers) return CDRGE_ERR_UNSUPPORTED;
+    if (int64_t(4) * f32_lds_floats(c->n_layers, c->vocab, c->embed, c->hidden, c->batch) > kMaxF32LdsBytes)
+      return CDRGE_ERR_UNSUPPORTED;
+    if (int64_t(4) * c->hidden >= (int64_t(1) << 30)) return CDRGE_ERR_UNSUPPORTED;
+  } else {
+    if (c->embed % 32 != 0 || c->hidden % kUnitsPerTile != 0 || c->vocab > kCeRows)
+      return CDRGE_ERR_UNSUPPORTED;
+    const int P = (c->probes_per_chunk == 0 || c->probes_per_chunk > c->n_probes) ? c->n_probes
+                                                                                 : c->probes_per_chunk;
+    if (int64_t(2) * P * c->batch >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+    if (P > 65535) return CDRGE_ERR_UNSUPPORTED;
+  }
+  return CDRGE_OK;
+}
+
+Plan make_plan(const cdrge_config* c) {
+  Plan p;
+  p.cfg = *c;
+  p.L = c->n_layers;
+  p.V = c->vocab;
+  p.E = c->embed;
+  p.H = c->hidden;
+  p.B = c->batch;
+  p.T = c->seq_len;
+  p.K = c->n_probes;
+  p.P = (c->probes_per_chunk == 0 || c->probes_per_chunk > c->n_probes) ? c->n_probes : c->probes_per_chunk;
+  int64_t off = 0;
+  auto add = [&](uint32_t id, int64_t rows, int64_t cols) {
+    p.tensors.push_back(TensorDesc{id, off, rows, cols});
+    off += rows * cols;
+  };
+  add(0, p.V, p.E);
+  for (int l = 0; l < p.L; ++l) {
+    add(1 + 3 * l, 4 * int64_t(p.H), (l == 0) ? p.E : p.H);
+    add(2 + 3 * l, 4 * int64_t(p.H), p.H);
+    add(3 + 3 * l, 1, 4 * int64_t(p.H));
+  }
+  add(1 + 3 * p.L, p.V, p.H);
+  add(2 + 3 * p.L, 1, p.V);
+  p.d = off;
+
+  const int64_t models = 2 * int64_t(p.P);
+  const int64_t ncols = models * p.B;
+  size_t w = 0;
+  auto region = [&](size_t bytes) {
+    const size_t at = w;
+    w = align_up(w + bytes);
+    return at;
+  };
+  p.off_flags = region(256);
+  p.off_seeds = region(sizeof(uint64_t) * p.K);
+  p.off_seq = region(sizeof(float) * models * p.B);
+  p.off_wp.assign(p.tensors.size(), 0);
+  p.off_wm.assign(p.tensors.size(), 0);
+  p.off_emb_m = p.off_bias_m = p.off_bout_m = p.off_h = p.off_c = 0;
+  if (c->dtype == CDRGE_BF16) {
+    for (const TensorDesc& t : p.tensors) {
+      const bool gemm = (t.id != 0) && (t.rows > 1);  // W_ih, W_hh, W_out
+      if (!gemm) continue;
+      p.off_wp[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
+      p.off_wm[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
+    }
+    p.off_emb_m = region(sizeof(uint16_t) * models * p.V * p.E);
+    p.off_bias_m = region(sizeof(float) * models * p.L * 4 * p.H);
+    p.off_bout_m = region(sizeof(float) * models * kCeRows);
+    p.off_h = region(sizeof(uint16_t) * int64_t(p.L) * 2 * ncols * p.H);
+    p.off_c = region(sizeof(float) * int64_t(p.L) * p.H * ncols);
+  }
+  p.total = w;
+  return p;
+}
+
+__global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
+
+}  // namespace
+
+struct cdrge_ctx {
+  Plan plan;
+  void* params = nullptr;
+  char* ws = nullptr;
+  hipStream_t stream = nullptr;
+  int device = 0;
+  bool timing = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[4];
+  std::vector<hipEvent_t> event_pool;
+  double total_ms[4] = {0, 0, 0, 0};
+  int64_t launches[4] = {0, 0, 0, 0};
+  double work[4] = {0, 0, 0, 0};
+
+  template <class T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(ws + off);
+  }
+
+  hipEvent_t get_event() {
+    if (!event_pool.empty()) {
+      hipEvent_t e = event_pool.back();
+      event_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+
+// Runs `launch` on the context's stream, timing it under `kind` when timing is enabled.
+template <class F>
+cdrge_status timed(cdrge_ctx* ctx, int kind, double work, F&& launch) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (ctx->timing) {
+    e0 = ctx->get_event();
+    e1 = ctx->get_event();
+    if (!e0 || !e1) return device_error("hipEventCreate", hipErrorOutOfMemory);
+    CDRGE_HIP(hipEventRecord(e0, ctx->stream));
+  }
+  launch();
+  CDRGE_HIP(hipGetLastError());
+  if (ctx->timing) {
+    CDRGE_HIP(hipEventRecord(e1, ctx->stream));
+    ctx->pending[kind].emplace_back(e0, e1);
+  }
+  ctx->work[kind] += work;
+  return CDRGE_OK;
+}
+
+#define CDRGE_TRY(expr)                   \
+  do {                                    \
+    const cdrge_status _s = (expr);       \
+    if (_s != CDRGE_OK) return _s;        \
+  } while (0)
+
+cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step,
+                                  float* losses, float* seq_losses) {
+  const Plan& p = ctx->plan;
+  const hipStream_t s = ctx->stream;
+  uint32_t* flags = ctx->at<uint32_t>(p.off_flags);
+  uint64_t* seeds = ctx->at<uint64_t>(p.off_seeds);
+  float* seq = ctx->at<float>(p.off_seq);
+  const float eps = p.cfg.eps;
+
+  CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+    hipLaunchKernelGGL(k_seeds, dim3((p.K + 255) / 256), dim3(256), 0, s, p.cfg.base_seed, step, p.K, seeds);
+  }));
+  CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+    hipLaunchKernelGGL(k_check_tokens, dim3(1), dim3(256), 0, s, tokens, p.B * (p.T + 1), p.V, flags);
+  }));
+
+  const bool bf16 = p.cfg.dtype == CDRGE_BF16;
+  if (bf16) {
+    const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
+    for (const TensorDesc& t : p.tensors) {
+      if (t.id == 0 || t.rows == 1) continue;
+      const int64_t n = t.rows * t.cols;
+      CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+        hipLaunchKernelGGL(k_pm_table_bf16, dim3(static_cast<uint32_t>((n / 8 + 256) / 256)), dim3(256), 0, s,
+                           theta + t.off, n, eps, ctx->at<uint16_t>(p.off_wp[t.id]),
+                           ctx->at<uint16_t>(p.off_wm[t.id]));
+      }));
+    }
+  }
+
+  for (int pair0 = 0; pair0 < p.K; pair0 += p.P) {
+    const int pc = (p.K - pair0 < p.P) ? (p.K - pair0) : p.P;
+    const int models = 2 * pc;
+    const int ncols = models * p.B;
+    if (!bf16) {
+      F32Model m;
+      m.theta = static_cast<const float*>(ctx->params);
+      m.off_emb = p.tensors[0].off;
+      for (int l = 0; l < p.L; ++l) {
+        m.off_wih[l] = p.tensors[1 + 3 * l].off;
+        m.off_whh[l] = p.tensors[2 + 3 * l].off;
+        m.off_b[l] = p.tensors[3 + 3 * l].off;
+      }
+      m.off_wout = p.tensors[1 + 3 * p.L].off;
+      m.off_bout = p.tensors[2 + 3 * p.L].off;
+      m.L = p.L; m.V = p.V; m.E = p.E; m.H = p.H; m.B = p.B; m.T = p.T;
+      const int S = p.B < kF32MaxSeq ? p.B : kF32MaxSeq;
+      const size_t lds = sizeof(float) * f32_lds_floats(p.L, p.V, p.E, p.H, p.B);
+      double flops = 0.0;
+      for (int l = 0; l < p.L; ++l)
+        flops += 2.0 * 4 * p.H * (((l == 0) ? p.E : p.H) + p.H);
+      flops = (flops + 2.0 * p.V * p.H) * double(ncols) * p.T;
+      CDRGE_TRY(timed(ctx, 0, flops, [&] {
+        hipLaunchKernelGGL(k_lstm_f32, dim3(pc, (p.B + S - 1) / S), dim3(kF32Threads), lds, s, m, tokens,
+                           seeds, pair0, eps, seq);
+      }));
+    } else {
+      const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
+      uint16_t* emb_m = ctx->at<uint16_t>(p.off_emb_m);
+      float* bias_m = ctx->at<float>(p.off_bias_m);
+      float* bout_m = ctx->at<float>(p.off_bout_m);
+      auto small = [&](const TensorDesc& t, int out_cols, uint16_t* ob, float* of) {
+        const int groups = static_cast<int>((t.cols + 31) / 32);
+        const int64_t n = int64_t(models) * t.rows * groups;
+        return timed(ctx, 3, 0.0, [&] {
+          hipLaunchKernelGGL(k_model_tensor_bf16, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s,
+                             theta + t.off, static_cast<int>(t.rows), static_cast<int>(t.cols), t.id, seeds,
+                             pair0, models, eps, out_cols, ob, of);
+        });
+      };
+      CDRGE_TRY(small(p.tensors[0], p.E, emb_m, nullptr));
+      for (int l = 0; l < p.L; ++l)
+        CDRGE_TRY(small(p.tensors[3 + 3 * l], p.L * 4 * p.H, nullptr, bias_m + int64_t(l) * 4 * p.H));
+      CDRGE_TRY(small(p.tensors[2 + 3 * p.L], kCeRows, nullptr, bout_m));
+
+      uint16_t* hbase = ctx->at<uint16_t>(p.off_h);
+      float* cbase = ctx->at<float>(p.off_c);
+      const int64_t ncols_max = 2 * int64_t(p.P) * p.B;
+      auto hbuf = [&](int l, int par) { return hbase + (int64_t(l) * 2 + par) * ncols_max * p.H; };
+      const dim3 ggrid(p.H / kUnitsPerTile, (p.B + kTileCols - 1) / kTileCols, pc);
+      const dim3 cgrid((p.B + kTileCols - 1) / kTileCols, pc);
+      for (int t = 0; t < p.T; ++t) {
+        for (int l = 0; l < p.L; ++l) {
+          GateArgs g;
+          const TensorDesc& tih = p.tensors[1 + 3 * l];
+          const TensorDesc& thh = p.tensors[2 + 3 * l];
+          g.wp_ih = ctx->at<uint16_t>(p.off_wp[tih.id]);
+          g.wm_ih = ctx->at<uint16_t>(p.off_wm[tih.id]);
+          g.wp_hh = ctx->at<uint16_t>(p.off_wp[thh.id]);
+          g.wm_hh = ctx->at<uint16_t>(p.off_wm[thh.id]);
+          g.emb_m = emb_m;
+          g.tokens = tokens;
+          g.x_h = (l == 0) ? nullptr : hbuf(l - 1, t & 1);
+          g.h_prev = hbuf(l, (t + 1) & 1);
+          g.h_out = hbuf(l, t & 1);
+          g.c = cbase + int64_t(l) * p.H * ncols_max;
+          g.bias_m = bias_m;
+          g.seeds = seeds;
+          g.pair0 = pair0;
+          g.in = static_cast<int>(tih.cols);
+          g.H = p.H; g.B = p.B; g.V = p.V; g.E = p.E; g.L = p.L;
+          g.layer = l; g.t = t; g.T = p.T; g.Ncols = ncols;
+          g.first = (t == 0) ? 1 : 0;
+          g.tensor_ih = tih.id;
+          g.tensor_hh = thh.id;
+          const double flops = 2.0 * 4 * p.H * double(g.in + (g.first ? 0 : p.H)) * ncols;
+          CDRGE_TRY(timed(ctx, 0, flops, [&] {
+            hipLaunchKernelGGL(k_lstm_gates_bf16, ggrid, dim3(kGateThreads), kGateLdsBytes, s, g);
+          }));
+        }
+        CeArgs ce;
+        const TensorDesc& tw = p.tensors[1 + 3 * p.L];
+        ce.wp = ctx->at<uint16_t>(p.off_wp[tw.id]);
+        ce.wm = ctx->at<uint16_t>(p.off_wm[tw.id]);
+        ce.h = hbuf(p.L - 1, t & 1);
+        ce.bout_m = bout_m;
+        ce.tokens = tokens;
+        ce.seeds = seeds;
+        ce.seq = seq;
+        ce.pair0 = pair0;
+        ce.H = p.H; ce.B = p.B; ce.V = p.V; ce.T = p.T; ce.t = t;
+        ce.tensor_wout = tw.id;
+        const double flops = 2.0 * p.V * p.H * double(ncols);
+        CDRGE_TRY(timed(ctx, 1, flops, [&] {
+          hipLaunchKernelGGL(k_logits_ce_bf16, cgrid, dim3(kGateThreads), kCeLdsBytes, s, ce);
+        }));
+      }
+    }
+    CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+      hipLaunchKernelGGL(k_loss_reduce, dim3(models), dim3(256), 0, s, seq, p.B, p.T, 2 * pair0, flags,
+                         losses, seq_losses);
+    }));
+  }
+  return CDRGE_OK;
+}
+
+cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) {
+  const Plan& p = ctx->plan;
+  const hipStream_t s = ctx->stream;
+  uint32_t* flags = ctx->at<uint32_t>(p.off_flags);
+  uint64_t* seeds = ctx->at<uint64_t>(p.off_seeds);
+  CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+    hipLaunchKernelGGL(k_seeds, dim3((p.K + 255) / 256), dim3(256), 0, s, p.cfg.base_seed, step, p.K, seeds);
+  }));
+  const float coef = static_cast<float>(static_cast<double>(p.cfg.lr) /
+                                        (2.0 * p.K * static_cast<double>(p.cfg.eps)));
+  const bool bf16 = p.cfg.dtype == CDRGE_BF16;
+  const size_t esz = bf16 ? 2 : 4;
+  for (const TensorDesc& t : p.tensors) {
+    const int64_t segs = t.rows * ((t.cols + 127) / 128);
+    const dim3 grid(static_cast<uint32_t>((segs + 15) / 16));
+    void* base = static_cast<char*>(ctx->params) + t.off * esz;
+    const double bytes = 2.0 * double(t.rows * t.cols) * esz;
+    CDRGE_TRY(timed(ctx, 2, bytes, [&] {
+      if (bf16)
+        hipLaunchKernelGGL(k_update<true>, grid, dim3(kUpdThreads), 0, s, base, static_cast<int>(t.rows),
+                           static_cast<int>(t.cols), t.id, seeds, losses, p.K, coef, flags);
+      else
+        hipLaunchKernelGGL(k_update<false>, grid, dim3(kUpdThreads), 0, s, base, static_cast<int>(t.rows),
+                           static_cast<int>(t.cols), t.id, seeds, losses, p.K, coef, flags);
+    }));
+  }
+  return CDRGE_OK;
+}
+
+cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
+  CDRGE_HIP(hipGetDevice(&ctx->device));
+  if (cfg->dtype == CDRGE_BF16) {
+    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_gates_bf16),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
+  } else {
+    const int lds = static_cast<int>(sizeof(float) * f32_lds_floats(cfg->n_layers, cfg->vocab, cfg->embed,
+                                                                    cfg->hidden, cfg->batch));
+    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_f32),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  }
+  uint32_t* flags = ctx->at<uint32_t>(ctx->plan.off_flags);
+  hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, ctx->stream, flags, 0u);
+  hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, ctx->stream, flags + 1, 0u);
+  CDRGE_HIP(hipGetLastError());
+  return CDRGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cdrge_last_error_detail(void) { return g_last_error; }
+
+int64_t cdrge_param_count(const cdrge_config* cfg) {
+  if (!basic_valid(cfg)) return -1;
+  return param_count(cfg);
+}
+
+cdrge_status cdrge_check_config(const cdrge_config* cfg) {
+  if (!basic_valid(cfg)) return CDRGE_ERR_INVALID_ARG;
+  return supported(cfg);
+}
+
+cdrge_status cdrge_workspace_bytes(const cdrge_config* cfg, size_t* bytes_out) {
+  if (!bytes_out) return CDRGE_ERR_INVALID_ARG;
+  const cdrge_status st = cdrge_check_config(cfg);
+  if (st != CDRGE_OK) return st;
+  *bytes_out = make_plan(cfg).total;
+  return CDRGE_OK;
+}
+
+cdrge_status cdrge_probe_seeds(const cdrge_config* cfg, uint64_t step, uint64_t* seeds_host) {
+  if (!basic_valid(cfg) || !seeds_host) return CDRGE_ERR_INVALID_ARG;
+  for (int i = 0; i < cfg->n_probes; ++i) seeds_host[i] = probe_seed(cfg->base_seed, step, static_cast<uint32_t>(i));
+  return CDRGE_OK;
+}
+
+cdrge_status cdrge_init(cdrge_ctx** ctx_out, const cdrge_config* cfg, void* params, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!ctx_out || !params) return CDRGE_ERR_INVALID_ARG;
+  *ctx_out = nullptr;
+  const cdrge_status st = cdrge_check_config(cfg);
+  if (st != CDRGE_OK) return st;
+  Plan plan = make_plan(cfg);
+  if (!workspace || workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return CDRGE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(params) % 16) != 0) return CDRGE_ERR_INVALID_ARG;
+  cdrge_ctx* ctx = new (std::nothrow) cdrge_ctx();
+  if (!ctx) return CDRGE_ERR_INVALID_ARG;
+  ctx->plan = std::move(plan);
+  ctx->params = params;
+  ctx->ws = static_cast<char*>(workspace);
+  ctx->stream = static_cast<hipStream_t>(stream);
+  const cdrge_status st2 = init_device(ctx, cfg);
+  if (st2 != CDRGE_OK) {
+    delete ctx;
+    return st2;
+  }
+  *ctx_out = ctx;
+  return CDRGE_OK;
+}
+
+cdrge_status cdrge_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step, float* losses,
+                                float* seq_losses) {
+  if (!ctx || !tokens || !losses) return CDRGE_ERR_INVALID_ARG;
+  return enqueue_probe_losses(ctx, tokens, step, losses, seq_losses);
+}
+
+cdrge_status cdrge_update(cdrge_ctx* ctx, uint64_t step, const float* losses) {
+  if (!ctx || !losses) return CDRGE_ERR_INVALID_ARG;
+  return enqueue_update(ctx, step, losses);
+}
+
+cdrge_status cdrge_step(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step, float* losses) {
+  if (!ctx || !tokens || !losses) return CDRGE_ERR_INVALID_ARG;
+  CDRGE_TRY(enqueue_probe_losses(ctx, tokens, step, losses, nullptr));
+  return enqueue_update(ctx, step, losses);
+}
+
+cdrge_status cdrge_sync_status(cdrge_ctx* ctx) {
+  if (!ctx) return CDRGE_ERR_INVALID_ARG;
+  CDRGE_HIP(hipStreamSynchronize(ctx->stream));
+  uint32_t flags[2] = {0, 0};
+  CDRGE_HIP(hipMemcpy(flags, ctx->at<uint32_t>(ctx->plan.off_flags), sizeof(flags), hipMemcpyDeviceToHost));
+  if (flags[0]) {
+    hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, ctx->stream, ctx->at<uint32_t>(ctx->plan.off_flags), 0u);
+    CDRGE_HIP(hipGetLastError());
+    CDRGE_HIP(hipStreamSynchronize(ctx->stream));
+    return CDRGE_ERR_NONFINITE;
+  }
+  return CDRGE_OK;
+}
+
+void cdrge_destroy(cdrge_ctx* ctx) {
+  if (!ctx) return;
+  for (auto& v : ctx->pending)
+    for (auto& pr : v) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+  for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+const char* cdrge_status_string(cdrge_status status) {
+  switch (status) {
+    case CDRGE_OK: return "CDRGE_OK";
+    case CDRGE_ERR_INVALID_ARG: return "CDRGE_ERR_INVALID_ARG";
+    case CDRGE_ERR_UNSUPPORTED: return "CDRGE_ERR_UNSUPPORTED";
+    case CDRGE_ERR_WORKSPACE: return "CDRGE_ERR_WORKSPACE";
+    case CDRGE_ERR_DEVICE: return "CDRGE_ERR_DEVICE";
+    case CDRGE_ERR_NONFINITE: return "CDRGE_ERR_NONFINITE";
+  }
+  return "CDRGE_UNKNOWN_STATUS";
+}
+
+cdrge_status cdrge_set_timing(cdrge_ctx* ctx, int enable) {
+  if (!ctx) return CDRGE_ERR_INVALID_ARG;
+  ctx->timing = enable != 0;
+  return CDRGE_OK;
+}
+
+cdrge_status cdrge_get_timing(cdrge_ctx* ctx, int kind, double* total_ms, int64_t* launches, int reset) {
+  if (!ctx || kind < 0 || kind > 3 || !total_ms || !launches) return CDRGE_ERR_INVALID_ARG;
+  CDRGE_HIP(hipStreamSynchronize(ctx->stream));
+  for (int k = 0; k < 4; ++k) {
+    for (auto& pr : ctx->pending[k]) {
+      float ms = 0.f;
+      CDRGE_HIP(hipEventElapsedTime(&ms, pr.first, pr.second));
+      ctx->total_ms[k] += ms;
+      ctx->launches[k] += 1;
+      ctx->event_pool.push_back(pr.first);
+      ctx->event_pool.push_back(pr.second);
+    }
+    ctx->pending[k].clear();
+  }
+  *total_ms = ctx->total_ms[kind];
+  *launches = ctx->launches[kind];
+  if (reset) {
+    for (int k = 0; k < 4; ++k) {
+      ctx->total_ms[k] = 0;
+      ctx->launches[k] = 0;
+      ctx->work[k] = 0;
+    }
+  }
+  return CDRGE_OK;
+}
+
+cdrge_status cdrge_get_work(cdrge_ctx* ctx, int kind, double* work) {
+  if (!ctx || kind < 0 || kind > 3 || !work) return CDRGE_ERR_INVALID_ARG;
+  *work = ctx->work[kind];
+  return CDRGE_OK;
+}
+
+}  // extern "C"
