@@ -89,7 +89,7 @@ int64_t cdrge_param_count(const cdrge_config* cfg);
 /* CDRGE_OK if the configuration is valid and supported; otherwise the reason.
  * Supported: F32 whenever one probe pair's recurrent state fits the on-chip buffers
  * (about 2 * B * (2 L H + 4 H + max(E, H)) floats <= 48K); BF16 when E % 32 == 0,
- * H % 64 == 0 and V <= 64. */
+ * H % 32 == 0 and V <= 64. */
 cdrge_status cdrge_check_config(const cdrge_config* cfg);
 
 /* Device workspace, in bytes, that cdrge_init needs for this configuration (256-byte aligned

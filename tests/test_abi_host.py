@@ -66,7 +66,7 @@ def test_config_validation(lib):
             setattr(c, k, v)
         assert b.cdrge_check_config(c) == 1, kw
         assert b.cdrge_param_count(c) == -1, kw
-    unsupported = [dict(embed=48), dict(hidden=96), dict(vocab=65), dict(n_probes=2048)]
+    unsupported = [dict(embed=48), dict(hidden=80), dict(vocab=65), dict(n_probes=2048)]
     for kw in unsupported:
         c = b.make_config(2, 50, 64, 128, 160, 3, 3, "bf16", 1e-4, 1e-4, 9)
         for k, v in kw.items():

@@ -187,3 +187,19 @@ def test_resume_equals_uninterrupted():
     run.update(2)
     np.testing.assert_array_equal(run.theta(), straight)
     run.close()
+
+
+def test_xcd_grouped_tile_order(oracle):
+    # H = 256 gives 8 row tiles and 32 pairs x 1 column block: the grid takes the XCD-grouped order.
+    c = b.make_config(1, 50, 64, 256, 256, 2, 32, "bf16", 1e-3, 1e-3, 82)
+    say("[gpu] xcd-grouped tile order")
+    theta, tokens = _inputs(c, 12)
+    run = GpuRun(c, theta, tokens)
+    losses, seq, st = run.probe_losses(0)
+    assert st == 0
+    probes, seqs = [0, 13, 31], [0, 1, 100, 255]
+    ref_l, ref_seq = oracle.probe_losses(ocfg(c), theta, tokens, 0, probe_ids=probes, seq_ids=seqs)
+    rows = [2 * i + s for i in probes for s in (0, 1)]
+    assert_losses_close(seq[np.ix_(rows, seqs)], ref_seq, 2e-2, "seq_losses")
+    np.testing.assert_allclose(losses, seq.astype(np.float64).sum(1) / (c.batch * c.seq_len), rtol=1e-6)
+    run.close()

@@ -14,6 +14,7 @@
 #include "kernels_bf16.h"
 #include "kernels_common.h"
 #include "kernels_f32.h"
+#include "kernels_gates_bf16.h"
 #include "philox.h"
 
 using namespace cdrge;
@@ -292,8 +293,13 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       float* cbase = ctx->at<float>(p.off_c);
       const int64_t ncols_max = 2 * int64_t(p.P) * p.B;
       auto hbuf = [&](int l, int par) { return hbase + (int64_t(l) * 2 + par) * ncols_max * p.H; };
-      const dim3 ggrid(p.H / kUnitsPerTile, (p.B + kTileCols - 1) / kTileCols, pc);
-      const dim3 cgrid((p.B + kTileCols - 1) / kTileCols, pc);
+      const int n_rt = p.H / kUnitsPerTile;
+      const int n_cb = (p.B + kTileCols - 1) / kTileCols;
+      const int n_blocks = n_rt * n_cb * pc;
+      // XCD-grouped order needs whole groups of 8 row tiles x 4 column blocks per XCD.
+      const int swizzle = (n_rt % 8 == 0) && ((n_cb * pc) % 4 == 0) && (n_blocks % 256 == 0);
+      const dim3 ggrid(n_blocks);
+      const dim3 cgrid((p.B + kCeCols - 1) / kCeCols, pc);
       for (int t = 0; t < p.T; ++t) {
         for (int l = 0; l < p.L; ++l) {
           GateArgs g;
@@ -318,6 +324,10 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           g.first = (t == 0) ? 1 : 0;
           g.tensor_ih = tih.id;
           g.tensor_hh = thh.id;
+          g.n_row_tiles = n_rt;
+          g.n_col_blocks = n_cb;
+          g.n_pairs = pc;
+          g.swizzle = swizzle;
           const double flops = 2.0 * 4 * p.H * double(g.in + (g.first ? 0 : p.H)) * ncols;
           CDRGE_TRY(timed(ctx, 0, flops, [&] {
             hipLaunchKernelGGL(k_lstm_gates_bf16, ggrid, dim3(kGateThreads), kGateLdsBytes, s, g);
@@ -337,7 +347,7 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
         ce.tensor_wout = tw.id;
         const double flops = 2.0 * p.V * p.H * double(ncols);
         CDRGE_TRY(timed(ctx, 1, flops, [&] {
-          hipLaunchKernelGGL(k_logits_ce_bf16, cgrid, dim3(kGateThreads), kCeLdsBytes, s, ce);
+          hipLaunchKernelGGL(k_logits_ce_bf16, cgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
         }));
       }
     }

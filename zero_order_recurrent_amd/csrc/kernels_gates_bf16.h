@@ -1,0 +1,298 @@
+// Perturbed LSTM gate product + fused cell update for bf16 models on gfx950 matrix cores.
+//
+// One launch per (layer, timestep) computes, for every probe pair of a chunk, the gate
+// pre-activations of both perturbed models (theta + eps p_i and theta - eps p_i),
+//   G = (W_ih +- eps P_ih) x_t + (W_hh +- eps P_hh) h_{t-1} + (b +- eps p_b),
+// and applies the LSTM cell to them in registers. This is the complete recurrent forward pass at
+// perturbed weights that the method evaluates (alex-wiki source note on arXiv 2505.17852,
+// "Method"), with Rademacher perturbations (pith.science review, "What carries the argument").
+//
+// The perturbed weight tile is never stored to memory: per step the probe-independent candidates
+// Wp = bf16(W + eps) and Wm = bf16(W - eps) exist once in memory, and each probe's tile is a
+// per-element bit select between them, driven by the probe's Philox sign bits, done in registers
+// on the way into LDS. Both models of a pair share the loaded candidates and the sign bits.
+//
+// Workgroup tile (256 threads = 4 waves of 64 lanes):
+//   rows    128 gate rows = 32 hidden units x 4 gates, interleaved (local row 4u + g is gate g of
+//           unit u) so that each lane's 16x16 accumulator holds all four gates of one unit;
+//   columns 256 batch columns of the +eps model and the same 256 of the -eps model;
+//   waves   (model, column half): each wave owns 128 x 128 = 8 x 8 MFMA 16x16x32 tiles
+//           (256 accumulator registers per lane);
+//   K loop  the concatenated reduction [x_t ; h_{t-1}] in chunks of 32, two LDS stages. The
+//           activation operand moves global -> LDS with direct 16-byte loads into an XOR-swizzled
+//           (bank-conflict-free) layout; the weight operand is loaded coalesced into registers,
+//           selected, and written to a padded LDS tile.
+// The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 8 row
+// tiles x 4 column blocks, which keeps their shared weight and activation chunks in that XCD's L2.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels_common.h"
+
+namespace cdrge {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGateThreads = 256;
+constexpr int kUnitsPerTile = 32;
+constexpr int kTileRows = 4 * kUnitsPerTile;   // 128 gate rows
+constexpr int kTileCols = 256;                 // batch columns per model
+constexpr int kKChunk = 32;
+constexpr int kAStride = 40;                   // bf16 per LDS row of the weight tile (32 + 8 pad)
+constexpr int kHsStride = 40;                  // bf16 per row of the h transpose buffer
+constexpr int kAStageElems = 2 * kTileRows * kAStride;        // both models
+constexpr int kBStageElems = 2 * kTileCols * kKChunk;         // 512 columns x 32, swizzled
+constexpr size_t kGateLdsBytes = sizeof(uint16_t) * 2 * (kAStageElems + kBStageElems);
+
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+__device__ __forceinline__ float fast_tanh(float x) { return 2.f * fast_sigmoid(2.f * x) - 1.f; }
+
+// Position of 16-byte piece p (k = 8p..8p+7) of activation column c inside an LDS stage: each
+// column takes 64 bytes and its pieces are XOR-swizzled so that 16 lanes reading the same piece
+// of 16 consecutive columns hit distinct banks.
+__device__ __forceinline__ int b_piece_offset(int c, int p) { return c * 64 + 16 * (p ^ ((c >> 1) & 3)); }
+
+struct GateArgs {
+  const uint16_t* wp_ih;
+  const uint16_t* wm_ih;   // [4H][in] candidates of W_ih
+  const uint16_t* wp_hh;
+  const uint16_t* wm_hh;   // [4H][H] candidates of W_hh
+  const uint16_t* emb_m;   // layer 0 input: per-model perturbed embedding [2P][V][E]
+  const int32_t* tokens;   // [B][T+1]
+  const uint16_t* x_h;     // layer > 0 input: previous layer's h_t, [Ncols][H]
+  const uint16_t* h_prev;  // this layer's h_{t-1}, [Ncols][H] (unused when first)
+  uint16_t* h_out;         // this layer's h_t, [Ncols][H]
+  float* c;                // this layer's cell state, [H][Ncols], updated in place
+  const float* bias_m;     // per-model perturbed gate bias [2P][L][4H]
+  const uint64_t* seeds;
+  int pair0, in, H, B, V, E, L, layer, t, T, Ncols, first;
+  int n_row_tiles, n_col_blocks, n_pairs, swizzle;
+  uint32_t tensor_ih, tensor_hh;
+};
+
+// Row tile / column block / pair of this workgroup (see the header comment for the XCD order).
+__device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, int& cb, int& pr) {
+  const int L = blockIdx.x;
+  int rtile, cw;
+  if (a.swizzle) {
+    const int n = gridDim.x;            // multiple of 8 * 32 when swizzling
+    const int v = (L & 7) * (n >> 3) + (L >> 3);
+    const int g = v >> 5, q = v & 31;
+    const int n_rg = a.n_row_tiles >> 3;
+    rtile = (g % n_rg) * 8 + (q & 7);
+    cw = (g / n_rg) * 4 + (q >> 3);
+  } else {
+    rtile = L % a.n_row_tiles;
+    cw = L / a.n_row_tiles;
+  }
+  rt = rtile;
+  cb = cw % a.n_col_blocks;
+  pr = cw / a.n_col_blocks;
+}
+
+__global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* As = smem;                           // [stage][model][128][40]
+  uint16_t* Bs = smem + 2 * kAStageElems;        // [stage][512 cols][32] swizzled
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int side = wave >> 1, chalf = wave & 1;
+  const int H = a.H;
+  int rt, cb, pr;
+  gate_tile_of_block(a, rt, cb, pr);
+  const int u0 = rt * kUnitsPerTile;
+  const int bcol0 = cb * kTileCols;
+  const uint64_t seed = a.seeds[a.pair0 + pr];
+
+  // ---- weight operand: thread owns local rows ra = tid/4 and rb = ra + 64, piece q = tid%4 ----
+  const int q = tid & 3;
+  const int ra = tid >> 2, rb = ra + 64;
+  const int grow_a = (ra & 3) * H + u0 + (ra >> 2);
+  const int grow_b = (rb & 3) * H + u0 + (rb >> 2);
+
+  // ---- activation operand: 8 direct 16-byte LDS loads per thread per chunk ----
+  // Load k of wave w fills bytes [(8w + k) * 1024, +1024) of the stage: lane l -> column
+  // (8w + k) * 16 + l / 4, stored slot l % 4, which holds piece (l % 4) ^ swizzle(column).
+  const uint16_t* xsrc[8];
+  const uint16_t* hsrc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = (8 * wave + k) * 16 + (lane >> 2);
+    const int p = (lane & 3) ^ ((c >> 1) & 3);
+    const int sd = c >> 8;
+    const int b = bcol0 + (c & 255);
+    const int bs = (b < a.B) ? b : 0;    // columns past the batch read column 0 (results unused)
+    const int m = 2 * pr + sd;
+    const int64_t gcol = static_cast<int64_t>(m) * a.B + bs;
+    if (a.layer == 0) {
+      int tok = a.tokens[static_cast<int64_t>(bs) * (a.T + 1) + a.t];
+      tok = min(max(tok, 0), a.V - 1);
+      xsrc[k] = a.emb_m + (static_cast<int64_t>(m) * a.V + tok) * a.E + 8 * p;
+    } else {
+      xsrc[k] = a.x_h + gcol * H + 8 * p;
+    }
+    hsrc[k] = a.h_prev + gcol * H + 8 * p;
+  }
+
+  const int kx = a.in / kKChunk;
+  const int kh = a.first ? 0 : H / kKChunk;
+  const int nch = kx + kh;
+
+  uint4 wpa, wma, wpb, wmb;  // staged weight candidates of the next chunk
+  PhiloxOut oa{0, 0, 0, 0}, ob{0, 0, 0, 0};
+
+  auto issue_b = [&](int c, int stage) {
+    const bool xpart = c < kx;
+    const int cc = xpart ? c : c - kx;
+    uint16_t* base = Bs + stage * kBStageElems + (8 * wave) * 512;  // 512 bf16 = 1024 bytes per load
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint16_t* src = (xpart ? xsrc[k] : hsrc[k]) + kKChunk * cc;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + k * 512), 16, 0, 0);
+    }
+  };
+  auto load_w = [&](int c) {
+    const bool xpart = c < kx;
+    const int cc = xpart ? c : c - kx;
+    const int ld = xpart ? a.in : H;
+    const uint16_t* wp = xpart ? a.wp_ih : a.wp_hh;
+    const uint16_t* wm = xpart ? a.wm_ih : a.wm_hh;
+    const int64_t off_a = static_cast<int64_t>(grow_a) * ld + kKChunk * cc + 8 * q;
+    const int64_t off_b = static_cast<int64_t>(grow_b) * ld + kKChunk * cc + 8 * q;
+    wpa = *reinterpret_cast<const uint4*>(wp + off_a);
+    wma = *reinterpret_cast<const uint4*>(wm + off_a);
+    wpb = *reinterpret_cast<const uint4*>(wp + off_b);
+    wmb = *reinterpret_cast<const uint4*>(wm + off_b);
+  };
+  // Selects the probe's weights for rows ra, rb of chunk c and writes both models' tiles to LDS.
+  auto form_w = [&](int c, int stage) {
+    const bool xpart = c < kx;
+    const int cc = xpart ? c : c - kx;
+    const uint32_t tensor = xpart ? a.tensor_ih : a.tensor_hh;
+    // Each lane of a row's quad evaluates Philox for a different 128-column block, once per 16
+    // chunks; the block of chunk cc is then broadcast from lane (cc/4) % 4 of the quad.
+    if ((cc & 15) == 0) {
+      const uint32_t blk = static_cast<uint32_t>((cc >> 2) + q);
+      oa = sign_block(seed, tensor, static_cast<uint32_t>(grow_a), blk);
+      ob = sign_block(seed, tensor, static_cast<uint32_t>(grow_b), blk);
+    }
+    const uint32_t wsel = static_cast<uint32_t>(cc & 3);
+    const int owner = (lane & ~3) | ((cc >> 2) & 3);
+    const uint32_t word_a = static_cast<uint32_t>(__shfl(static_cast<int>(pick_word(oa, wsel)), owner));
+    const uint32_t word_b = static_cast<uint32_t>(__shfl(static_cast<int>(pick_word(ob, wsel)), owner));
+    // Piece q covers columns 8q..8q+7 of the 32-column word: pairs 4q..4q+3, which read bits
+    // 4q+p (even column) and 16+4q+p (odd column).
+    const uint32_t ta = word_a >> (4 * q), tb = word_b >> (4 * q);
+    const uint32_t pa[4] = {wpa.x, wpa.y, wpa.z, wpa.w}, ma[4] = {wma.x, wma.y, wma.z, wma.w};
+    const uint32_t pb[4] = {wpb.x, wpb.y, wpb.z, wpb.w}, mb[4] = {wmb.x, wmb.y, wmb.z, wmb.w};
+    uint32_t plus_a[4], minus_a[4], plus_b[4], minus_b[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // bits p and p+16 moved to 15 and 31, then replicated over each half-word
+      const uint32_t mka = __builtin_amdgcn_perm(0u, ta << (15 - p), 0x09090808u);
+      const uint32_t mkb = __builtin_amdgcn_perm(0u, tb << (15 - p), 0x09090808u);
+      plus_a[p] = (mka & ma[p]) | (~mka & pa[p]);   // sign -1: +eps model takes w - eps
+      minus_a[p] = (mka & pa[p]) | (~mka & ma[p]);
+      plus_b[p] = (mkb & mb[p]) | (~mkb & pb[p]);
+      minus_b[p] = (mkb & pb[p]) | (~mkb & mb[p]);
+    }
+    uint16_t* st = As + stage * kAStageElems;
+    *reinterpret_cast<uint4*>(st + (0 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(plus_a[0], plus_a[1], plus_a[2], plus_a[3]);
+    *reinterpret_cast<uint4*>(st + (1 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(minus_a[0], minus_a[1], minus_a[2], minus_a[3]);
+    *reinterpret_cast<uint4*>(st + (0 * kTileRows + rb) * kAStride + 8 * q) = make_uint4(plus_b[0], plus_b[1], plus_b[2], plus_b[3]);
+    *reinterpret_cast<uint4*>(st + (1 * kTileRows + rb) * kAStride + 8 * q) = make_uint4(minus_b[0], minus_b[1], minus_b[2], minus_b[3]);
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mma = [&](int stage) {
+    const uint16_t* A = As + stage * kAStageElems + (side * kTileRows + (lane & 15)) * kAStride + 8 * (lane >> 4);
+    const char* Bb = reinterpret_cast<const char*>(Bs + stage * kBStageElems);
+    bf16x8 bfr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 256 * side + 128 * chalf + 16 * j + (lane & 15);
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bb + b_piece_offset(c, lane >> 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 afr = *reinterpret_cast<const bf16x8*>(A + 16 * i * kAStride);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Prologue: chunk 0 into stage 0.
+  issue_b(0, 0);
+  load_w(0);
+  form_w(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int cur = c & 1, nxt = cur ^ 1;
+    const bool more = c + 1 < nch;
+    if (more) {
+      issue_b(c + 1, nxt);
+      load_w(c + 1);
+    }
+    mma(cur);
+    if (more) form_w(c + 1, nxt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- fused LSTM cell; h leaves through LDS as whole 64-byte column segments ----------------
+  uint16_t* Hs = smem;  // [512 columns][40], reused after the K loop
+  const int m = 2 * pr + side;
+  const int G = 4 * H;
+  const float* bias = a.bias_m + (static_cast<int64_t>(m) * a.L + a.layer) * G;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ul = 4 * i + (lane >> 4);
+    const int u = u0 + ul;
+    const float bi = bias[u], bf = bias[H + u], bg = bias[2 * H + u], bo = bias[3 * H + u];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cl = 128 * chalf + 16 * j + (lane & 15);
+      const int b = bcol0 + cl;
+      if (b < a.B) {
+        const int64_t gcol = static_cast<int64_t>(m) * a.B + b;
+        const float ig = fast_sigmoid(acc[i][j][0] + bi);
+        const float fg = fast_sigmoid(acc[i][j][1] + bf);
+        const float gg = fast_tanh(acc[i][j][2] + bg);
+        const float og = fast_sigmoid(acc[i][j][3] + bo);
+        float* cp = a.c + static_cast<int64_t>(u) * a.Ncols + gcol;
+        const float cprev = a.first ? 0.f : *cp;
+        const float cn = fg * cprev + ig * gg;
+        *cp = cn;
+        const float hv = og * fast_tanh(cn);
+        Hs[(256 * side + cl) * kHsStride + ul] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int cidx = 2 * tid + k;  // 0..511
+    const int sd = cidx >> 8;
+    const int b = bcol0 + (cidx & 255);
+    if (b < a.B) {
+      const int64_t gcol = static_cast<int64_t>(2 * pr + sd) * a.B + b;
+      const uint4* src = reinterpret_cast<const uint4*>(Hs + cidx * kHsStride);
+      uint4* dst = reinterpret_cast<uint4*>(a.h_out + gcol * H + u0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v] = src[v];
+    }
+  }
+}
+
+}  // namespace cdrge

@@ -69,9 +69,15 @@ def make_tokens(p: Preset) -> np.ndarray:
 
 
 def make_theta_f32(p: Preset, d: int) -> np.ndarray:
+    # Drawn in slices (same stream as one draw of d values) to bound the float64 temporaries.
     rng = np.random.default_rng(2000 + p.index)
     bound = 1.0 / np.sqrt(p.hidden)
-    return rng.uniform(-bound, bound, size=d).astype(np.float32)
+    out = np.empty(d, dtype=np.float32)
+    step = 1 << 25
+    for s in range(0, d, step):
+        n = min(step, d - s)
+        out[s:s + n] = rng.uniform(-bound, bound, size=n)
+    return out
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
