@@ -89,7 +89,10 @@ cdrge_status supported(const cdrge_config* c) {
       return CDRGE_ERR_UNSUPPORTED;
     const int P = (c->probes_per_chunk == 0 || c->probes_per_chunk > c->n_probes) ? c->n_probes
                                                                                  : c->probes_per_chunk;
-    if (int64_t(2) * P * c->batch >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+    if (int64_t(2) * P * c->batch * c->hidden >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+    if (int64_t(2) * P * c->vocab * c->embed >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+    if (int64_t(4) * c->hidden * (c->embed > c->hidden ? c->embed : c->hidden) >= (int64_t(1) << 31))
+      return CDRGE_ERR_UNSUPPORTED;
     if (P > 65535) return CDRGE_ERR_UNSUPPORTED;
   }
   return CDRGE_OK;

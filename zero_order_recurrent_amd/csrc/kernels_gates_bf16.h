@@ -12,16 +12,18 @@
 // per-element bit select between them, driven by the probe's Philox sign bits, done in registers
 // on the way into LDS. Both models of a pair share the loaded candidates and the sign bits.
 //
-// Workgroup tile (256 threads = 4 waves of 64 lanes):
+// Workgroup tile (512 threads = 8 waves of 64 lanes, two per SIMD):
 //   rows    128 gate rows = 32 hidden units x 4 gates, interleaved (local row 4u + g is gate g of
 //           unit u) so that each lane's 16x16 accumulator holds all four gates of one unit;
 //   columns 256 batch columns of the +eps model and the same 256 of the -eps model;
-//   waves   (model, column half): each wave owns 128 x 128 = 8 x 8 MFMA 16x16x32 tiles
-//           (256 accumulator registers per lane);
-//   K loop  the concatenated reduction [x_t ; h_{t-1}] in chunks of 32, two LDS stages. The
-//           activation operand moves global -> LDS with direct 16-byte loads into an XOR-swizzled
-//           (bank-conflict-free) layout; the weight operand is loaded coalesced into registers,
-//           selected, and written to a padded LDS tile.
+//   waves   (model, column quarter): each wave owns 128 x 64 = 8 x 4 MFMA 16x16x32 tiles
+//           (128 accumulator registers per lane); the two waves of a SIMD overlap one's weight
+//           select work with the other's MFMAs;
+//   K loop  the concatenated reduction [x_t ; h_{t-1}] in chunks of 32. The activation operand
+//           moves global -> LDS with direct 16-byte loads into an XOR-swizzled (bank-conflict-free)
+//           three-stage ring, issued two chunks ahead; the weight candidates of the next chunk are
+//           loaded coalesced into registers before the current chunk's MFMAs, then selected and
+//           written to a padded two-stage LDS tile.
 // The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 8 row
 // tiles x 4 column blocks, which keeps their shared weight and activation chunks in that XCD's L2.
 #pragma once
@@ -35,7 +37,7 @@ namespace cdrge {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGateThreads = 256;
+constexpr int kGateThreads = 512;
 constexpr int kUnitsPerTile = 32;
 constexpr int kTileRows = 4 * kUnitsPerTile;   // 128 gate rows
 constexpr int kTileCols = 256;                 // batch columns per model
@@ -44,7 +46,9 @@ constexpr int kAStride = 40;                   // bf16 per LDS row of the weight
 constexpr int kHsStride = 40;                  // bf16 per row of the h transpose buffer
 constexpr int kAStageElems = 2 * kTileRows * kAStride;        // both models
 constexpr int kBStageElems = 2 * kTileCols * kKChunk;         // 512 columns x 32, swizzled
-constexpr size_t kGateLdsBytes = sizeof(uint16_t) * 2 * (kAStageElems + kBStageElems);
+constexpr int kAStages = 2;
+constexpr int kBStages = 3;
+constexpr size_t kGateLdsBytes = sizeof(uint16_t) * (kAStages * kAStageElems + kBStages * kBStageElems);
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
@@ -96,11 +100,11 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
 
 __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                           // [stage][model][128][40]
-  uint16_t* Bs = smem + 2 * kAStageElems;        // [stage][512 cols][32] swizzled
+  uint16_t* As = smem;                                 // [2 stages][model][128][40]
+  uint16_t* Bs = smem + kAStages * kAStageElems;       // [3 stages][512 cols][32] swizzled
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int side = wave >> 1, chalf = wave & 1;
+  const int side = wave >> 2, cq = wave & 3;
   const int H = a.H;
   int rt, cb, pr;
   gate_tile_of_block(a, rt, cb, pr);
@@ -108,181 +112,195 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   const int bcol0 = cb * kTileCols;
   const uint64_t seed = a.seeds[a.pair0 + pr];
 
-  // ---- weight operand: thread owns local rows ra = tid/4 and rb = ra + 64, piece q = tid%4 ----
+  // ---- weight operand: thread owns local row ra = tid/4 (4 lanes per row), piece q = tid%4 ----
   const int q = tid & 3;
-  const int ra = tid >> 2, rb = ra + 64;
-  const int grow_a = (ra & 3) * H + u0 + (ra >> 2);
-  const int grow_b = (rb & 3) * H + u0 + (rb >> 2);
+  const int ra = tid >> 2;
+  const int grow = (ra & 3) * H + u0 + (ra >> 2);
 
-  // ---- activation operand: 8 direct 16-byte LDS loads per thread per chunk ----
-  // Load k of wave w fills bytes [(8w + k) * 1024, +1024) of the stage: lane l -> column
-  // (8w + k) * 16 + l / 4, stored slot l % 4, which holds piece (l % 4) ^ swizzle(column).
-  const uint16_t* xsrc[8];
-  const uint16_t* hsrc[8];
+  // ---- activation operand: 4 direct 16-byte LDS loads per thread per chunk ----
+  // Load k of wave w fills bytes [(4w + k) * 1024, +1024) of the stage: lane l -> column
+  // (4w + k) * 16 + l / 4, stored slot l % 4, which holds piece (l % 4) ^ swizzle(column).
+  // Element offsets are 32-bit (the host guarantees Ncols * H and 2P * V * E fit) from uniform bases.
+  const uint16_t* xbase = (a.layer == 0) ? a.emb_m : a.x_h;
+  uint32_t xoff[4], hoff[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int c = (8 * wave + k) * 16 + (lane >> 2);
+  for (int k = 0; k < 4; ++k) {
+    const int c = (4 * wave + k) * 16 + (lane >> 2);
     const int p = (lane & 3) ^ ((c >> 1) & 3);
     const int sd = c >> 8;
     const int b = bcol0 + (c & 255);
     const int bs = (b < a.B) ? b : 0;    // columns past the batch read column 0 (results unused)
     const int m = 2 * pr + sd;
-    const int64_t gcol = static_cast<int64_t>(m) * a.B + bs;
+    const uint32_t gcol = static_cast<uint32_t>(m * a.B + bs);
     if (a.layer == 0) {
       int tok = a.tokens[static_cast<int64_t>(bs) * (a.T + 1) + a.t];
       tok = min(max(tok, 0), a.V - 1);
-      xsrc[k] = a.emb_m + (static_cast<int64_t>(m) * a.V + tok) * a.E + 8 * p;
+      xoff[k] = static_cast<uint32_t>((m * a.V + tok) * a.E + 8 * p);
     } else {
-      xsrc[k] = a.x_h + gcol * H + 8 * p;
+      xoff[k] = gcol * static_cast<uint32_t>(H) + 8 * p;
     }
-    hsrc[k] = a.h_prev + gcol * H + 8 * p;
+    hoff[k] = gcol * static_cast<uint32_t>(H) + 8 * p;
   }
 
   const int kx = a.in / kKChunk;
   const int kh = a.first ? 0 : H / kKChunk;
   const int nch = kx + kh;
 
-  uint4 wpa, wma, wpb, wmb;  // staged weight candidates of the next chunk
-  PhiloxOut oa{0, 0, 0, 0}, ob{0, 0, 0, 0};
+  uint4 wpr, wmr;  // weight candidates of row ra for the next chunk
+  PhiloxOut oa{0, 0, 0, 0};
 
   auto issue_b = [&](int c, int stage) {
     const bool xpart = c < kx;
     const int cc = xpart ? c : c - kx;
-    uint16_t* base = Bs + stage * kBStageElems + (8 * wave) * 512;  // 512 bf16 = 1024 bytes per load
+    uint16_t* base = Bs + stage * kBStageElems + (4 * wave) * 512;  // 512 bf16 = 1024 bytes per load
+    const uint16_t* src = xpart ? xbase : a.h_prev;
+    const uint32_t kofs = static_cast<uint32_t>(kKChunk * cc);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint16_t* src = (xpart ? xsrc[k] : hsrc[k]) + kKChunk * cc;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + k * 512), 16, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t off = (xpart ? xoff[k] : hoff[k]) + kofs;
+      __builtin_amdgcn_global_load_lds(src + off, (__attribute__((address_space(3))) void*)(base + k * 512), 16, 0, 0);
     }
   };
-  auto load_w = [&](int c) {
+  auto load_w = [&](int c, uint4& wp_out, uint4& wm_out) {
     const bool xpart = c < kx;
     const int cc = xpart ? c : c - kx;
     const int ld = xpart ? a.in : H;
     const uint16_t* wp = xpart ? a.wp_ih : a.wp_hh;
     const uint16_t* wm = xpart ? a.wm_ih : a.wm_hh;
-    const int64_t off_a = static_cast<int64_t>(grow_a) * ld + kKChunk * cc + 8 * q;
-    const int64_t off_b = static_cast<int64_t>(grow_b) * ld + kKChunk * cc + 8 * q;
-    wpa = *reinterpret_cast<const uint4*>(wp + off_a);
-    wma = *reinterpret_cast<const uint4*>(wm + off_a);
-    wpb = *reinterpret_cast<const uint4*>(wp + off_b);
-    wmb = *reinterpret_cast<const uint4*>(wm + off_b);
+    const uint32_t off = static_cast<uint32_t>(grow * ld + kKChunk * cc + 8 * q);
+    wp_out = *reinterpret_cast<const uint4*>(wp + off);
+    wm_out = *reinterpret_cast<const uint4*>(wm + off);
   };
-  // Selects the probe's weights for rows ra, rb of chunk c and writes both models' tiles to LDS.
-  auto form_w = [&](int c, int stage) {
+  // Philox words of the 128-column blocks used by chunks cc..cc+15 of a tensor: each lane of a
+  // row's quad evaluates a different block (one call per lane per 16 chunks).
+  auto philox_w = [&](int c) {
     const bool xpart = c < kx;
     const int cc = xpart ? c : c - kx;
-    const uint32_t tensor = xpart ? a.tensor_ih : a.tensor_hh;
-    // Each lane of a row's quad evaluates Philox for a different 128-column block, once per 16
-    // chunks; the block of chunk cc is then broadcast from lane (cc/4) % 4 of the quad.
     if ((cc & 15) == 0) {
-      const uint32_t blk = static_cast<uint32_t>((cc >> 2) + q);
-      oa = sign_block(seed, tensor, static_cast<uint32_t>(grow_a), blk);
-      ob = sign_block(seed, tensor, static_cast<uint32_t>(grow_b), blk);
+      const uint32_t tensor = xpart ? a.tensor_ih : a.tensor_hh;
+      oa = sign_block(seed, tensor, static_cast<uint32_t>(grow), static_cast<uint32_t>((cc >> 2) + q));
     }
-    const uint32_t wsel = static_cast<uint32_t>(cc & 3);
-    const int owner = (lane & ~3) | ((cc >> 2) & 3);
-    const uint32_t word_a = static_cast<uint32_t>(__shfl(static_cast<int>(pick_word(oa, wsel)), owner));
-    const uint32_t word_b = static_cast<uint32_t>(__shfl(static_cast<int>(pick_word(ob, wsel)), owner));
+  };
+  // Selects the probe's weights for row ra of chunk c and writes both models' tiles to LDS.
+  // The word of chunk c is word (cc & 3) of the block; the lanes keep their four words rotating by
+  // one position per chunk (reset by philox_w), so it is always .x - no data-dependent selects.
+  auto form_w = [&](int c, const uint4& wpv, const uint4& wmv, int stage) {
+    const bool xpart = c < kx;
+    const int cc = xpart ? c : c - kx;
+    const int owner = (lane & ~3) | ((cc >> 2) & 3);  // the quad lane holding this block
+    const uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(oa.x), owner));
+    oa = PhiloxOut{oa.y, oa.z, oa.w, oa.x};
     // Piece q covers columns 8q..8q+7 of the 32-column word: pairs 4q..4q+3, which read bits
     // 4q+p (even column) and 16+4q+p (odd column).
-    const uint32_t ta = word_a >> (4 * q), tb = word_b >> (4 * q);
-    const uint32_t pa[4] = {wpa.x, wpa.y, wpa.z, wpa.w}, ma[4] = {wma.x, wma.y, wma.z, wma.w};
-    const uint32_t pb[4] = {wpb.x, wpb.y, wpb.z, wpb.w}, mb[4] = {wmb.x, wmb.y, wmb.z, wmb.w};
-    uint32_t plus_a[4], minus_a[4], plus_b[4], minus_b[4];
+    const uint32_t t4 = word >> (4 * q);
+    const uint32_t pv[4] = {wpv.x, wpv.y, wpv.z, wpv.w}, mv[4] = {wmv.x, wmv.y, wmv.z, wmv.w};
+    uint32_t plus[4], minus[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       // bits p and p+16 moved to 15 and 31, then replicated over each half-word
-      const uint32_t mka = __builtin_amdgcn_perm(0u, ta << (15 - p), 0x09090808u);
-      const uint32_t mkb = __builtin_amdgcn_perm(0u, tb << (15 - p), 0x09090808u);
-      plus_a[p] = (mka & ma[p]) | (~mka & pa[p]);   // sign -1: +eps model takes w - eps
-      minus_a[p] = (mka & pa[p]) | (~mka & ma[p]);
-      plus_b[p] = (mkb & mb[p]) | (~mkb & pb[p]);
-      minus_b[p] = (mkb & pb[p]) | (~mkb & mb[p]);
+      const uint32_t mk = __builtin_amdgcn_perm(0u, t4 << (15 - p), 0x09090808u);
+      plus[p] = (mk & mv[p]) | (~mk & pv[p]);   // sign -1: +eps model takes w - eps
+      minus[p] = (mk & pv[p]) | (~mk & mv[p]);
     }
     uint16_t* st = As + stage * kAStageElems;
-    *reinterpret_cast<uint4*>(st + (0 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(plus_a[0], plus_a[1], plus_a[2], plus_a[3]);
-    *reinterpret_cast<uint4*>(st + (1 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(minus_a[0], minus_a[1], minus_a[2], minus_a[3]);
-    *reinterpret_cast<uint4*>(st + (0 * kTileRows + rb) * kAStride + 8 * q) = make_uint4(plus_b[0], plus_b[1], plus_b[2], plus_b[3]);
-    *reinterpret_cast<uint4*>(st + (1 * kTileRows + rb) * kAStride + 8 * q) = make_uint4(minus_b[0], minus_b[1], minus_b[2], minus_b[3]);
+    *reinterpret_cast<uint4*>(st + (0 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(plus[0], plus[1], plus[2], plus[3]);
+    *reinterpret_cast<uint4*>(st + (1 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(minus[0], minus[1], minus[2], minus[3]);
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mma = [&](int stage) {
-    const uint16_t* A = As + stage * kAStageElems + (side * kTileRows + (lane & 15)) * kAStride + 8 * (lane >> 4);
-    const char* Bb = reinterpret_cast<const char*>(Bs + stage * kBStageElems);
-    bf16x8 bfr[8];
+  auto mma = [&](int astage, int bstage) {
+    const uint16_t* A = As + astage * kAStageElems + (side * kTileRows + (lane & 15)) * kAStride + 8 * (lane >> 4);
+    const char* Bb = reinterpret_cast<const char*>(Bs + bstage * kBStageElems);
+    bf16x8 bfr[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 256 * side + 128 * chalf + 16 * j + (lane & 15);
-      bfr[j] = *reinterpret_cast<const bf16x8*>(Bb + b_piece_offset(c, lane >> 4));
+    for (int j = 0; j < 4; ++j) {
+      const int cidx = 256 * side + 64 * cq + 16 * j + (lane & 15);
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bb + b_piece_offset(cidx, lane >> 4));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bf16x8 afr = *reinterpret_cast<const bf16x8*>(A + 16 * i * kAStride);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
     }
   };
 
-  // Prologue: chunk 0 into stage 0.
+  // One K step: chunk c is multiplied (A stage c&1, B stage c%3) while the loads of chunk c+1's
+  // weights and chunk c+2's activations are in flight; then chunk c+1 is selected into A stage
+  // (c+1)&1. The issue sequence has no branches (past the last chunk it reloads the last chunk
+  // into a stage that is not read again, and the select writes an unused A stage), so at the
+  // wait exactly the 4 activation loads of step c may still be outstanding.
+  auto kstep = [&](int c) {
+    load_w(min(c + 1, nch - 1), wpr, wmr);
+    __builtin_amdgcn_sched_barrier(0);  // weights strictly before activations (wait accounting)
+    issue_b(min(c + 2, nch - 1), (c + 2) % kBStages);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    mma(c & 1, c % kBStages);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    philox_w(c + 1);
+    form_w(c + 1, wpr, wmr, (c + 1) & 1);
+    __syncthreads();
+  };
+
+  // Prologue: activations of chunks 0 and 1 in flight, chunk 0 selected into A stage 0.
   issue_b(0, 0);
-  load_w(0);
-  form_w(0, 0);
+  load_w(0, wpr, wmr);
+  if (nch > 1) {
+    issue_b(1, 1);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  philox_w(0);
+  form_w(0, wpr, wmr, 0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) kstep(c);
+  // The last steps leave activation loads in flight; LDS is reused below.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int cur = c & 1, nxt = cur ^ 1;
-    const bool more = c + 1 < nch;
-    if (more) {
-      issue_b(c + 1, nxt);
-      load_w(c + 1);
-    }
-    mma(cur);
-    if (more) form_w(c + 1, nxt);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
 
   // ---- fused LSTM cell; h leaves through LDS as whole 64-byte column segments ----------------
   uint16_t* Hs = smem;  // [512 columns][40], reused after the K loop
   const int m = 2 * pr + side;
   const int G = 4 * H;
   const float* bias = a.bias_m + (static_cast<int64_t>(m) * a.L + a.layer) * G;
+  const uint32_t ncols = static_cast<uint32_t>(a.Ncols);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ul = 4 * i + (lane >> 4);
     const int u = u0 + ul;
     const float bi = bias[u], bf = bias[H + u], bg = bias[2 * H + u], bo = bias[3 * H + u];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int cl = 128 * chalf + 16 * j + (lane & 15);
+    for (int j = 0; j < 4; ++j) {
+      const int cl = 64 * cq + 16 * j + (lane & 15);
       const int b = bcol0 + cl;
       if (b < a.B) {
-        const int64_t gcol = static_cast<int64_t>(m) * a.B + b;
+        const uint32_t gcol = static_cast<uint32_t>(m * a.B + b);
         const float ig = fast_sigmoid(acc[i][j][0] + bi);
         const float fg = fast_sigmoid(acc[i][j][1] + bf);
         const float gg = fast_tanh(acc[i][j][2] + bg);
         const float og = fast_sigmoid(acc[i][j][3] + bo);
-        float* cp = a.c + static_cast<int64_t>(u) * a.Ncols + gcol;
-        const float cprev = a.first ? 0.f : *cp;
+        const uint32_t coff = static_cast<uint32_t>(u) * ncols + gcol;  // < H * Ncols < 2^31
+        const float cprev = a.first ? 0.f : a.c[coff];
         const float cn = fg * cprev + ig * gg;
-        *cp = cn;
+        a.c[coff] = cn;
         const float hv = og * fast_tanh(cn);
         Hs[(256 * side + cl) * kHsStride + ul] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
       }
     }
+    // one unit row at a time: keeps the cell loads of later rows from being hoisted here
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int cidx = 2 * tid + k;  // 0..511
+  {
+    const int cidx = tid;  // 0..511
     const int sd = cidx >> 8;
     const int b = bcol0 + (cidx & 255);
     if (b < a.B) {
