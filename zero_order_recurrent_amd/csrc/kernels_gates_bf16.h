@@ -48,17 +48,41 @@ constexpr int kAStageElems = 2 * kTileRows * kAStride;        // both models
 constexpr int kBStageElems = 2 * kTileCols * kKChunk;         // 512 columns x 32, swizzled
 constexpr int kAStages = 2;
 constexpr int kBStages = 3;
-constexpr size_t kGateLdsBytes = sizeof(uint16_t) * (kAStages * kAStageElems + kBStages * kBStageElems);
+constexpr size_t kGateBiasOffset = sizeof(uint16_t) * (kAStages * kAStageElems + kBStages * kBStageElems);
+constexpr size_t kGateLdsBytes = kGateBiasOffset + sizeof(float) * 2 * 4 * kUnitsPerTile;  // + gate biases
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 __device__ __forceinline__ float fast_tanh(float x) { return 2.f * fast_sigmoid(2.f * x) - 1.f; }
 
+// LSTM cell from the four gate pre-activations, with the reciprocals merged:
+//   sigmoid(x) = 1/(1+e^-x), tanh(x) = (1-e^-2x)/(1+e^-2x),
+//   c' = c sigmoid(f) + sigmoid(i) tanh(g) = (c A Gm + Gp F) / (F A Gm),
+//   h  = sigmoid(o) tanh(c') = (1 - e^-2c') / (O (1 + e^-2c')),
+// with A = 1+e^-i, F = 1+e^-f, Gp/Gm = 1 -/+ e^-2g, O = 1+e^-o. Arguments are clamped to
+// [-15, 15] (sigmoid(-15) = 3e-7, tanh(15) = 1 in float), which bounds every product below 1e27;
+// the clamp is written with comparisons so that a NaN argument stays NaN.
+__device__ __forceinline__ float clamp15(float x) { return x < -15.f ? -15.f : (x > 15.f ? 15.f : x); }
+__device__ __forceinline__ void lstm_cell(float gi, float gf, float gg, float go, float c, float& c_out,
+                                          float& h_out) {
+  const float A = 1.f + __expf(-clamp15(gi));
+  const float F = 1.f + __expf(-clamp15(gf));
+  const float eg = __expf(-2.f * clamp15(gg));
+  const float O = 1.f + __expf(-clamp15(go));
+  const float Gm = 1.f + eg, Gp = 1.f - eg;
+  const float AG = A * Gm;
+  const float cn = (c * AG + Gp * F) * __builtin_amdgcn_rcpf(F * AG);
+  const float ec = __expf(-2.f * clamp15(cn));
+  c_out = cn;
+  h_out = (1.f - ec) * __builtin_amdgcn_rcpf(O * (1.f + ec));
+}
+
 // Position of 16-byte piece p (k = 8p..8p+7) of activation column c inside an LDS stage: each
-// column takes 64 bytes and its pieces are XOR-swizzled so that 16 lanes reading the same piece
-// of 16 consecutive columns hit distinct banks.
-__device__ __forceinline__ int b_piece_offset(int c, int p) { return c * 64 + 16 * (p ^ ((c >> 1) & 3)); }
+// column takes 64 bytes and its pieces are XOR-swizzled with (c >> 2) & 3, so that the 16 lanes
+// of one LDS phase, reading the same piece of 16 consecutive columns, cover all 64 banks once.
+__device__ __forceinline__ int b_swizzle(int c) { return (c >> 2) & 3; }
+__device__ __forceinline__ int b_piece_offset(int c, int p) { return c * 64 + 16 * (p ^ b_swizzle(c)); }
 
 struct GateArgs {
   const uint16_t* wp_ih;
@@ -126,7 +150,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int c = (4 * wave + k) * 16 + (lane >> 2);
-    const int p = (lane & 3) ^ ((c >> 1) & 3);
+    const int p = (lane & 3) ^ b_swizzle(c);
     const int sd = c >> 8;
     const int b = bcol0 + (c & 255);
     const int bs = (b < a.B) ? b : 0;    // columns past the batch read column 0 (results unused)
@@ -216,19 +240,19 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   auto mma = [&](int astage, int bstage) {
     const uint16_t* A = As + astage * kAStageElems + (side * kTileRows + (lane & 15)) * kAStride + 8 * (lane >> 4);
     const char* Bb = reinterpret_cast<const char*>(Bs + bstage * kBStageElems);
-    bf16x8 bfr[4];
+    bf16x8 afr[8], bfr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cidx = 256 * side + 64 * cq + 16 * j + (lane & 15);
       bfr[j] = *reinterpret_cast<const bf16x8*>(Bb + b_piece_offset(cidx, lane >> 4));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x8 afr = *reinterpret_cast<const bf16x8*>(A + 16 * i * kAStride);
+    for (int i = 0; i < 8; ++i) afr[i] = *reinterpret_cast<const bf16x8*>(A + 16 * i * kAStride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
   // One K step: chunk c is multiplied (A stage c&1, B stage c%3) while the loads of chunk c+1's
@@ -249,6 +273,26 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     __syncthreads();
   };
 
+  // Gate biases of both models for the tile's 32 units, [model][gate][unit], into LDS.
+  float* bias_s = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + kGateBiasOffset);
+  if (tid < 2 * 4 * kUnitsPerTile) {
+    const int sd = tid >> 7, g = (tid >> 5) & 3, u = tid & 31;
+    bias_s[tid] = a.bias_m[(static_cast<int64_t>(2 * pr + sd) * a.L + a.layer) * (4 * H) + g * H + u0 + u];
+  }
+  // Cell state of this lane's 8 x 4 cells, loaded now so its latency hides under the K loop.
+  const int m_out = 2 * pr + side;
+  const uint32_t ncols = static_cast<uint32_t>(a.Ncols);
+  float cst[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = bcol0 + 64 * cq + 16 * j + (lane & 15);
+      const uint32_t coff = static_cast<uint32_t>(u0 + 4 * i + (lane >> 4)) * ncols +
+                            static_cast<uint32_t>(m_out * a.B + (b < a.B ? b : 0));
+      cst[i][j] = a.first ? 0.f : a.c[coff];
+    }
+
   // Prologue: activations of chunks 0 and 1 in flight, chunk 0 selected into A stage 0.
   issue_b(0, 0);
   load_w(0, wpr, wmr);
@@ -268,35 +312,24 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
 
   // ---- fused LSTM cell; h leaves through LDS as whole 64-byte column segments ----------------
   uint16_t* Hs = smem;  // [512 columns][40], reused after the K loop
-  const int m = 2 * pr + side;
-  const int G = 4 * H;
-  const float* bias = a.bias_m + (static_cast<int64_t>(m) * a.L + a.layer) * G;
-  const uint32_t ncols = static_cast<uint32_t>(a.Ncols);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ul = 4 * i + (lane >> 4);
     const int u = u0 + ul;
-    const float bi = bias[u], bf = bias[H + u], bg = bias[2 * H + u], bo = bias[3 * H + u];
+    const float* bs = bias_s + side * 4 * kUnitsPerTile + ul;
+    const float bi = bs[0], bf = bs[kUnitsPerTile], bg = bs[2 * kUnitsPerTile], bo = bs[3 * kUnitsPerTile];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cl = 64 * cq + 16 * j + (lane & 15);
       const int b = bcol0 + cl;
       if (b < a.B) {
-        const uint32_t gcol = static_cast<uint32_t>(m * a.B + b);
-        const float ig = fast_sigmoid(acc[i][j][0] + bi);
-        const float fg = fast_sigmoid(acc[i][j][1] + bf);
-        const float gg = fast_tanh(acc[i][j][2] + bg);
-        const float og = fast_sigmoid(acc[i][j][3] + bo);
-        const uint32_t coff = static_cast<uint32_t>(u) * ncols + gcol;  // < H * Ncols < 2^31
-        const float cprev = a.first ? 0.f : a.c[coff];
-        const float cn = fg * cprev + ig * gg;
+        const uint32_t coff = static_cast<uint32_t>(u) * ncols + static_cast<uint32_t>(m_out * a.B + b);
+        float cn, hv;
+        lstm_cell(acc[i][j][0] + bi, acc[i][j][1] + bf, acc[i][j][2] + bg, acc[i][j][3] + bo, cst[i][j], cn, hv);
         a.c[coff] = cn;
-        const float hv = og * fast_tanh(cn);
         Hs[(256 * side + cl) * kHsStride + ul] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
       }
     }
-    // one unit row at a time: keeps the cell loads of later rows from being hoisted here
-    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   {
