@@ -85,3 +85,87 @@ def test_param_count_and_layout(oracle):
     for L, E, H, V, d in big:
         cfg = OracleConfig(L, V, E, H, 1, 1, 1, "f32", 1e-3, 1e-3, 1)
         assert oracle.param_count(cfg) == d
+
+
+def _bf16_round(x: torch.Tensor) -> torch.Tensor:
+    """float64 -> nearest bf16 (through float32, ties to even) -> float64, by torch's own casts."""
+    return x.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def torch_bf16_seq_losses(oracle, cfg, weights64, tokens):
+    """The bf16 model of the oracle rebuilt from torch's LSTMCell, F.linear and F.cross_entropy in
+    float64: weights are the given (bf16-valued) numbers, and every activation is rounded to bf16
+    where it enters a matrix product - h into W_hh, into the next layer's W_ih and into W_out."""
+    lay = {tid: (off, rows, cols) for tid, off, rows, cols in oracle.layout(cfg)}
+
+    def tensor(tid):
+        off, rows, cols = lay[tid]
+        return torch.from_numpy(weights64[off:off + rows * cols].reshape(rows, cols).copy())
+
+    L, H, B = cfg.n_layers, cfg.hidden, cfg.batch
+    cells = []
+    with torch.no_grad():
+        for l in range(L):
+            cell = torch.nn.LSTMCell(cfg.embed if l == 0 else H, H, dtype=torch.float64)
+            cell.weight_ih.copy_(tensor(1 + 3 * l))
+            cell.weight_hh.copy_(tensor(2 + 3 * l))
+            cell.bias_ih.copy_(tensor(3 + 3 * l).reshape(-1))
+            cell.bias_hh.zero_()
+            cells.append(cell)
+        tok = torch.from_numpy(tokens.astype(np.int64))
+        emb = tensor(0)
+        h = [torch.zeros(B, H, dtype=torch.float64) for _ in range(L)]
+        c = [torch.zeros(B, H, dtype=torch.float64) for _ in range(L)]
+        total = torch.zeros(B, dtype=torch.float64)
+        for t in range(cfg.seq_len):
+            x = emb[tok[:, t]]
+            for l in range(L):
+                h[l], c[l] = cells[l](x, (_bf16_round(h[l]), c[l]))
+                x = _bf16_round(h[l])
+            logits = torch.nn.functional.linear(x, tensor(1 + 3 * L), tensor(2 + 3 * L).reshape(-1))
+            total += torch.nn.functional.cross_entropy(logits, tok[:, t + 1], reduction="none")
+        return total.numpy()
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f64(u: np.ndarray) -> np.ndarray:
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("shape", SHAPES[:2])
+def test_bf16_forward_matches_torch_cells_with_rounded_activations(oracle, shape):
+    cfg = _cfg(shape, storage="bf16")
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(23)
+    w16 = _bf16_bits(rng.uniform(-0.6, 0.6, d))
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    got = oracle.seq_losses(cfg, w16, tokens, round_act_bf16=True)
+    ref = torch_bf16_seq_losses(oracle, cfg, _bits_to_f64(w16), tokens)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=0)
+    # the rounding points matter: without them the losses move far beyond the tolerance
+    unrounded = oracle.seq_losses(cfg, w16, tokens, round_act_bf16=False)
+    assert np.max(np.abs(unrounded - ref) / np.abs(ref)) > 1e-6
+
+
+def test_bf16_probe_losses_match_torch(oracle):
+    """Perturbed bf16 forwards: theta' = bf16(float(w) + float(s eps) p) formed with torch's
+    rounding from the oracle's probe vector (itself pinned to rocRAND's Philox and the sign
+    mapping), then the torch model above. Covers the oracle's perturbed copy and its bf16 forward."""
+    shape = SHAPES[1]
+    cfg = OracleConfig(n_probes=3, storage="bf16", eps=1e-2, lr=1e-2, base_seed=77, **shape)
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(24)
+    w16 = _bf16_bits(rng.uniform(-0.3, 0.3, d))
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    step = 5
+    _, seq = oracle.probe_losses(cfg, w16, tokens, step)
+    w32 = torch.from_numpy(_bits_to_f64(w16).astype(np.float32))
+    for i in range(cfg.n_probes):
+        p = torch.from_numpy(oracle.probe_vector(cfg, oracle.probe_seed(cfg.base_seed, step, i)).astype(np.float32))
+        for side, sgn in enumerate((1.0, -1.0)):
+            pert = (w32 + torch.tensor(sgn * cfg.eps, dtype=torch.float32) * p).to(torch.bfloat16)
+            ref = torch_bf16_seq_losses(oracle, cfg, pert.to(torch.float64).numpy(), tokens)
+            np.testing.assert_allclose(seq[2 * i + side], ref, rtol=1e-12, atol=0)
