@@ -53,8 +53,10 @@ struct Plan {
   int L, V, E, H, B, T, K, P;
   int64_t d;
   std::vector<TensorDesc> tensors;  // index == tensor id
-  size_t off_flags, off_seeds, off_seq, off_emb_m, off_bias_m, off_bout_m, off_h, off_c, total;
+  size_t off_flags, off_seeds, off_seq, off_emb_m, off_bias_m, off_bout_m, off_x0, off_h, off_c, total;
+  int64_t ncols_pad, n_tiles;  // bf16: padded column count of the activation buffers; gate tiles per chunk
   std::vector<size_t> off_wp, off_wm;  // per tensor id (bf16 matrices only)
+  std::vector<size_t> off_sg;          // per tensor id (bf16 W_ih, W_hh): sign words of a chunk
 };
 
 bool basic_valid(const cdrge_config* c) {
@@ -89,7 +91,8 @@ cdrge_status supported(const cdrge_config* c) {
       return CDRGE_ERR_UNSUPPORTED;
     const int P = (c->probes_per_chunk == 0 || c->probes_per_chunk > c->n_probes) ? c->n_probes
                                                                                  : c->probes_per_chunk;
-    if (int64_t(2) * P * c->batch * c->hidden >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+    const int64_t maxdim = c->embed > c->hidden ? c->embed : c->hidden;
+    if ((int64_t(2) * P * c->batch + kTileCols) * maxdim >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
     if (int64_t(2) * P * c->vocab * c->embed >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
     if (int64_t(4) * c->hidden * (c->embed > c->hidden ? c->embed : c->hidden) >= (int64_t(1) << 31))
       return CDRGE_ERR_UNSUPPORTED;
@@ -137,7 +140,10 @@ Plan make_plan(const cdrge_config* c) {
   p.off_seq = region(sizeof(float) * models * p.B);
   p.off_wp.assign(p.tensors.size(), 0);
   p.off_wm.assign(p.tensors.size(), 0);
-  p.off_emb_m = p.off_bias_m = p.off_bout_m = p.off_h = p.off_c = 0;
+  p.off_sg.assign(p.tensors.size(), 0);
+  p.off_emb_m = p.off_bias_m = p.off_bout_m = p.off_x0 = p.off_h = p.off_c = 0;
+  p.ncols_pad = ncols + kTileCols;
+  p.n_tiles = int64_t(p.H / kUnitsPerTile) * ((p.B + kTileCols - 1) / kTileCols) * p.P;
   if (c->dtype == CDRGE_BF16) {
     for (const TensorDesc& t : p.tensors) {
       const bool gemm = (t.id != 0) && (t.rows > 1);  // W_ih, W_hh, W_out
@@ -145,11 +151,15 @@ Plan make_plan(const cdrge_config* c) {
       p.off_wp[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
       p.off_wm[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
     }
+    for (int l = 0; l < p.L; ++l)
+      for (const TensorDesc& t : {p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]})
+        p.off_sg[t.id] = region(sizeof(uint32_t) * p.P * t.rows * (t.cols / 32));
     p.off_emb_m = region(sizeof(uint16_t) * models * p.V * p.E);
     p.off_bias_m = region(sizeof(float) * models * p.L * 4 * p.H);
     p.off_bout_m = region(sizeof(float) * models * kCeRows);
-    p.off_h = region(sizeof(uint16_t) * int64_t(p.L) * 2 * ncols * p.H);
-    p.off_c = region(sizeof(float) * int64_t(p.L) * p.H * ncols);
+    p.off_x0 = region(sizeof(uint16_t) * p.ncols_pad * p.E);
+    p.off_h = region(sizeof(uint16_t) * int64_t(p.L) * 2 * p.ncols_pad * p.H);
+    p.off_c = region(sizeof(float) * int64_t(p.L) * p.n_tiles * kGateThreads * 32);
   }
   p.total = w;
   return p;
@@ -291,19 +301,37 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       for (int l = 0; l < p.L; ++l)
         CDRGE_TRY(small(p.tensors[3 + 3 * l], p.L * 4 * p.H, nullptr, bias_m + int64_t(l) * 4 * p.H));
       CDRGE_TRY(small(p.tensors[2 + 3 * p.L], kCeRows, nullptr, bout_m));
+      for (int l = 0; l < p.L; ++l)
+        for (const TensorDesc& t : {p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]}) {
+          const int wpr = static_cast<int>(t.cols / 32);
+          const int64_t n = int64_t(pc) * t.rows * ((wpr + 3) / 4);
+          CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+            hipLaunchKernelGGL(k_sign_words, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, seeds,
+                               pair0, pc, t.id, static_cast<int>(t.rows), wpr, ctx->at<uint32_t>(p.off_sg[t.id]));
+          }));
+        }
 
       uint16_t* hbase = ctx->at<uint16_t>(p.off_h);
+      uint16_t* x0 = ctx->at<uint16_t>(p.off_x0);
       float* cbase = ctx->at<float>(p.off_c);
-      const int64_t ncols_max = 2 * int64_t(p.P) * p.B;
-      auto hbuf = [&](int l, int par) { return hbase + (int64_t(l) * 2 + par) * ncols_max * p.H; };
+      auto hbuf = [&](int l, int par) { return hbase + (int64_t(l) * 2 + par) * p.ncols_pad * p.H; };
       const int n_rt = p.H / kUnitsPerTile;
       const int n_cb = (p.B + kTileCols - 1) / kTileCols;
       const int n_blocks = n_rt * n_cb * pc;
-      // XCD-grouped order needs whole groups of 8 row tiles x 4 column blocks per XCD.
-      const int swizzle = (n_rt % 8 == 0) && ((n_cb * pc) % 4 == 0) && (n_blocks % 256 == 0);
+      // The XCD-grouped order needs whole groups of kGroupRows row tiles x kGroupCols column
+      // blocks on each of the 8 XCDs.
+      const int swizzle = (n_rt % kGroupRows == 0) && ((n_cb * pc) % kGroupCols == 0) &&
+                          (n_blocks % (8 * kGroupRows * kGroupCols) == 0);
       const dim3 ggrid(n_blocks);
       const dim3 cgrid((p.B + kCeCols - 1) / kCeCols, pc);
       for (int t = 0; t < p.T; ++t) {
+        {
+          const int64_t n = int64_t(ncols + kTileCols) * (p.E / 8);
+          CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+            hipLaunchKernelGGL(k_gather_x0, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, emb_m,
+                               tokens, p.B, p.T, t, p.V, p.E, ncols, ncols + kTileCols, x0);
+          }));
+        }
         for (int l = 0; l < p.L; ++l) {
           GateArgs g;
           const TensorDesc& tih = p.tensors[1 + 3 * l];
@@ -312,21 +340,17 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           g.wm_ih = ctx->at<uint16_t>(p.off_wm[tih.id]);
           g.wp_hh = ctx->at<uint16_t>(p.off_wp[thh.id]);
           g.wm_hh = ctx->at<uint16_t>(p.off_wm[thh.id]);
-          g.emb_m = emb_m;
-          g.tokens = tokens;
-          g.x_h = (l == 0) ? nullptr : hbuf(l - 1, t & 1);
+          g.sg_ih = ctx->at<uint32_t>(p.off_sg[tih.id]);
+          g.sg_hh = ctx->at<uint32_t>(p.off_sg[thh.id]);
+          g.x_in = (l == 0) ? x0 : hbuf(l - 1, t & 1);
           g.h_prev = hbuf(l, (t + 1) & 1);
           g.h_out = hbuf(l, t & 1);
-          g.c = cbase + int64_t(l) * p.H * ncols_max;
+          g.c_tile = cbase + int64_t(l) * p.n_tiles * kGateThreads * 32;
           g.bias_m = bias_m;
-          g.seeds = seeds;
-          g.pair0 = pair0;
           g.in = static_cast<int>(tih.cols);
-          g.H = p.H; g.B = p.B; g.V = p.V; g.E = p.E; g.L = p.L;
-          g.layer = l; g.t = t; g.T = p.T; g.Ncols = ncols;
+          g.H = p.H; g.B = p.B; g.L = p.L;
+          g.layer = l;
           g.first = (t == 0) ? 1 : 0;
-          g.tensor_ih = tih.id;
-          g.tensor_hh = thh.id;
           g.n_row_tiles = n_rt;
           g.n_col_blocks = n_cb;
           g.n_pairs = pc;

@@ -77,6 +77,30 @@ __global__ void k_pm_table_bf16(const uint16_t* __restrict__ w, int64_t n, float
   }
 }
 
+// The probe sign bits of one recurrent weight tensor [rows][cols] (cols a multiple of 32) for
+// the probe pairs pair0 .. pair0 + pc - 1 of a chunk, as 32-bit words in column order:
+// out[q][r][w] covers columns 32w .. 32w + 31 of row r and is word (w & 3) of the Philox block
+// w >> 2, so bit ((c & 31) >> 1) | ((c & 1) << 4) of word c >> 5 is the sign bit of column c.
+// The gate kernels read one word per row and 32-column chunk instead of regenerating the same
+// Philox blocks for every timestep and column tile. One thread per (pair, row, 128-column block).
+__global__ void k_sign_words(const uint64_t* __restrict__ seeds, int pair0, int pc, uint32_t tensor,
+                             int rows, int wpr, uint32_t* __restrict__ out) {
+  const int nblk = (wpr + 3) / 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(pc) * rows * nblk) return;
+  const int blk = static_cast<int>(i % nblk);
+  const int64_t qr = i / nblk;
+  const int r = static_cast<int>(qr % rows);
+  const int q = static_cast<int>(qr / rows);
+  const PhiloxOut o = sign_block(seeds[pair0 + q], tensor, static_cast<uint32_t>(r), static_cast<uint32_t>(blk));
+  uint32_t* dst = out + qr * wpr + 4 * blk;
+  const int nw = min(4, wpr - 4 * blk);
+  const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k < nw) dst[k] = w[k];
+}
+
 // Per-model perturbed copy of a small tensor [rows][cols] of a bf16 model, for models
 // m = 0..2P-1 of a chunk (model 2q is probe pair0+q at +eps, 2q+1 the same probe at -eps).
 // out_bf16 (if not null) gets bf16 bits at [m][r][out_cols]; out_f32 (if not null) gets the same
@@ -104,6 +128,27 @@ __global__ void k_model_tensor_bf16(const uint16_t* __restrict__ src, int rows, 
     if (out_bf16) out_bf16[o_idx] = static_cast<uint16_t>(v);
     if (out_f32) out_f32[o_idx] = bf16_to_f32(v);
   }
+}
+
+// Layer-0 input of timestep t for every (model, sequence) column of a chunk:
+// x[m * B + b][:] = emb_m[m][token(b, t)][:], the model's perturbed embedding row, so that the
+// gate kernel reads its input operand as [columns][E] exactly like the h of a lower layer.
+// Columns ncols .. ncols_pad - 1 are zero. Tokens outside [0, V) are clamped (the step's losses
+// are NaN then anyway). One thread per 16-byte piece (E % 8 == 0).
+__global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* __restrict__ tokens, int B,
+                            int T, int t, int V, int E, int ncols, int ncols_pad, uint16_t* __restrict__ x) {
+  const int pieces = E / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(ncols_pad) * pieces) return;
+  const int col = static_cast<int>(i / pieces), pc = static_cast<int>(i % pieces);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (col < ncols) {
+    const int m = col / B, b = col % B;
+    int tok = tokens[static_cast<int64_t>(b) * (T + 1) + t];
+    tok = min(max(tok, 0), V - 1);
+    v = reinterpret_cast<const uint4*>(emb_m + (static_cast<int64_t>(m) * V + tok) * E)[pc];
+  }
+  reinterpret_cast<uint4*>(x + static_cast<int64_t>(col) * E)[pc] = v;
 }
 
 // losses[m0 + m] = (sum_b seq[m][b]) / (B T) with a fixed-order double reduction (bitwise

@@ -17,18 +17,22 @@
 //           unit u) so that each lane's 16x16 accumulator holds all four gates of one unit;
 //   columns 256 batch columns of the +eps model and the same 256 of the -eps model;
 //   waves   (model, column quarter): each wave owns 128 x 64 = 8 x 4 MFMA 16x16x32 tiles
-//           (128 accumulator registers per lane); the two waves of a SIMD overlap one's weight
-//           select work with the other's MFMAs;
-//   K loop  the concatenated reduction [x_t ; h_{t-1}] in chunks of 32. The activation operand
-//           moves global -> LDS with direct 16-byte loads into an XOR-swizzled (bank-conflict-free)
-//           three-stage ring, issued two chunks ahead; the weight candidates of the next chunk are
-//           loaded coalesced into registers before the current chunk's MFMAs, then selected and
-//           written to a padded two-stage LDS tile.
+//           (128 accumulator registers per lane).
+// K loop over the concatenated reduction [x_t ; h_{t-1}] in chunks of 32, software-pipelined:
+//   * activations go straight from global memory into the MFMA operand registers of the wave
+//     that uses them (each column belongs to one wave), two chunks ahead, in a 3-deep ring;
+//   * the selected weight tiles of both models live in a 3-stage LDS ring. While chunk c is
+//     multiplied, every wave reads its fragments of chunk c+1 (row group i right after the MFMAs
+//     that last use row group i of chunk c), and the workgroup selects chunk c+2 into the third
+//     stage; one barrier per chunk, placed right after that select, orders it all;
+//   * the weight candidates of chunk c+2 are loaded coalesced one chunk before they are selected.
 // The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 8 row
 // tiles x 4 column blocks, which keeps their shared weight and activation chunks in that XCD's L2.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kernels_common.h"
 
@@ -42,14 +46,18 @@ constexpr int kUnitsPerTile = 32;
 constexpr int kTileRows = 4 * kUnitsPerTile;   // 128 gate rows
 constexpr int kTileCols = 256;                 // batch columns per model
 constexpr int kKChunk = 32;
-constexpr int kAStride = 40;                   // bf16 per LDS row of the weight tile (32 + 8 pad)
 constexpr int kHsStride = 40;                  // bf16 per row of the h transpose buffer
-constexpr int kAStageElems = 2 * kTileRows * kAStride;        // both models
-constexpr int kBStageElems = 2 * kTileCols * kKChunk;         // 512 columns x 32, swizzled
-constexpr int kAStages = 2;
-constexpr int kBStages = 3;
-constexpr size_t kGateBiasOffset = sizeof(uint16_t) * (kAStages * kAStageElems + kBStages * kBStageElems);
+constexpr int kAStageBytes = 2 * kTileRows * 64;   // both models' 128 x 32 bf16 tiles
+constexpr int kAStages = 4;
+constexpr int kBRing = 4;                          // activation register ring (chunks)
+// Workgroups resident on one XCD at a time (one per CU) cover kGroupRows row tiles x kGroupCols
+// column blocks, so that each activation chunk is fetched into that XCD's L2 once for kGroupRows
+// workgroups and each weight chunk once for kGroupCols.
+constexpr int kGroupRows = 8, kGroupCols = 4;
+constexpr size_t kGateBiasOffset = size_t(kAStages) * kAStageBytes;
 constexpr size_t kGateLdsBytes = kGateBiasOffset + sizeof(float) * 2 * 4 * kUnitsPerTile;  // + gate biases
+static_assert(sizeof(uint16_t) * 2 * kTileCols * kHsStride <= kGateBiasOffset,
+              "the h transpose buffer reuses the weight ring");
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
@@ -78,28 +86,26 @@ __device__ __forceinline__ void lstm_cell(float gi, float gf, float gg, float go
   h_out = (1.f - ec) * __builtin_amdgcn_rcpf(O * (1.f + ec));
 }
 
-// Position of 16-byte piece p (k = 8p..8p+7) of activation column c inside an LDS stage: each
-// column takes 64 bytes and its pieces are XOR-swizzled with (c >> 2) & 3, so that the 16 lanes
-// of one LDS phase, reading the same piece of 16 consecutive columns, cover all 64 banks once.
-__device__ __forceinline__ int b_swizzle(int c) { return (c >> 2) & 3; }
-__device__ __forceinline__ int b_piece_offset(int c, int p) { return c * 64 + 16 * (p ^ b_swizzle(c)); }
+// Byte offset of 16-byte piece p (k = 8p..8p+7) of row r in a tile of 64-byte rows. Pieces are
+// XOR-swizzled with (r >> 2) & 3: the 16 lanes of one LDS phase - 16 consecutive rows at one
+// piece (fragment reads) or 4 rows x 4 pieces (select writes) - touch 16 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int piece_offset(int r, int p) { return r * 64 + 16 * (p ^ ((r >> 2) & 3)); }
 
 struct GateArgs {
   const uint16_t* wp_ih;
   const uint16_t* wm_ih;   // [4H][in] candidates of W_ih
   const uint16_t* wp_hh;
   const uint16_t* wm_hh;   // [4H][H] candidates of W_hh
-  const uint16_t* emb_m;   // layer 0 input: per-model perturbed embedding [2P][V][E]
-  const int32_t* tokens;   // [B][T+1]
-  const uint16_t* x_h;     // layer > 0 input: previous layer's h_t, [Ncols][H]
-  const uint16_t* h_prev;  // this layer's h_{t-1}, [Ncols][H] (unused when first)
-  uint16_t* h_out;         // this layer's h_t, [Ncols][H]
-  float* c;                // this layer's cell state, [H][Ncols], updated in place
+  const uint32_t* sg_ih;   // sign words of W_ih for the chunk's pairs, [pairs][4H][in / 32]
+  const uint32_t* sg_hh;   // sign words of W_hh, [pairs][4H][H / 32]
+  const uint16_t* x_in;    // input of this layer at t, [columns][in] (padded columns readable)
+  const uint16_t* h_prev;  // this layer's h_{t-1}, [columns][H] (unused when first)
+  uint16_t* h_out;         // this layer's h_t, [columns][H]
+  float* c_tile;           // this layer's cell state in accumulator order, 64 KB per tile
   const float* bias_m;     // per-model perturbed gate bias [2P][L][4H]
-  const uint64_t* seeds;
-  int pair0, in, H, B, V, E, L, layer, t, T, Ncols, first;
+  int in, H, B, L, layer, first;
   int n_row_tiles, n_col_blocks, n_pairs, swizzle;
-  uint32_t tensor_ih, tensor_hh;
 };
 
 // Row tile / column block / pair of this workgroup (see the header comment for the XCD order).
@@ -107,12 +113,15 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
   const int L = blockIdx.x;
   int rtile, cw;
   if (a.swizzle) {
-    const int n = gridDim.x;            // multiple of 8 * 32 when swizzling
+    // Workgroups are dealt to the 8 XCDs round-robin; v enumerates one XCD's workgroups in
+    // dispatch order, and each run of kGroupRows * kGroupCols of them covers kGroupRows row tiles
+    // x kGroupCols column blocks (the host checks the divisibility this needs).
+    const int n = gridDim.x;
     const int v = (L & 7) * (n >> 3) + (L >> 3);
-    const int g = v >> 5, q = v & 31;
-    const int n_rg = a.n_row_tiles >> 3;
-    rtile = (g % n_rg) * 8 + (q & 7);
-    cw = (g / n_rg) * 4 + (q >> 3);
+    const int g = v / (kGroupRows * kGroupCols), q = v % (kGroupRows * kGroupCols);
+    const int n_rg = a.n_row_tiles / kGroupRows;
+    rtile = (g % n_rg) * kGroupRows + q % kGroupRows;
+    cw = (g / n_rg) * kGroupCols + q / kGroupRows;
   } else {
     rtile = L % a.n_row_tiles;
     cw = L / a.n_row_tiles;
@@ -124,96 +133,54 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
 
 __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                                 // [2 stages][model][128][40]
-  uint16_t* Bs = smem + kAStages * kAStageElems;       // [3 stages][512 cols][32] swizzled
+  char* As = reinterpret_cast<char*>(smem);  // [4 stages][model][128 rows][64 B], swizzled
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int side = wave >> 2, cq = wave & 3;
   const int H = a.H;
   int rt, cb, pr;
   gate_tile_of_block(a, rt, cb, pr);
   const int u0 = rt * kUnitsPerTile;
   const int bcol0 = cb * kTileCols;
-  const uint64_t seed = a.seeds[a.pair0 + pr];
+  const int m_out = 2 * pr + side;
 
-  // ---- weight operand: thread owns local row ra = tid/4 (4 lanes per row), piece q = tid%4 ----
+  // ---- weight select: thread owns local row ra = tid/4 (4 lanes per row), piece q = tid%4 ----
   const int q = tid & 3;
   const int ra = tid >> 2;
   const int grow = (ra & 3) * H + u0 + (ra >> 2);
+  const uint32_t woff_x = static_cast<uint32_t>(grow * a.in + 8 * q);
+  const uint32_t woff_h = static_cast<uint32_t>(grow * H + 8 * q);
+  // sign words of row grow for this pair: one 32-bit word per 32-column chunk
+  const uint32_t* sgx = a.sg_ih + (static_cast<int64_t>(pr) * 4 * H + grow) * (a.in / kKChunk);
+  const uint32_t* sgh = a.sg_hh + (static_cast<int64_t>(pr) * 4 * H + grow) * (H / kKChunk);
 
-  // ---- activation operand: 4 direct 16-byte LDS loads per thread per chunk ----
-  // Load k of wave w fills bytes [(4w + k) * 1024, +1024) of the stage: lane l -> column
-  // (4w + k) * 16 + l / 4, stored slot l % 4, which holds piece (l % 4) ^ swizzle(column).
-  // Element offsets are 32-bit (the host guarantees Ncols * H and 2P * V * E fit) from uniform bases.
-  const uint16_t* xbase = (a.layer == 0) ? a.emb_m : a.x_h;
-  uint32_t xoff[4], hoff[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = (4 * wave + k) * 16 + (lane >> 2);
-    const int p = (lane & 3) ^ b_swizzle(c);
-    const int sd = c >> 8;
-    const int b = bcol0 + (c & 255);
-    const int bs = (b < a.B) ? b : 0;    // columns past the batch read column 0 (results unused)
-    const int m = 2 * pr + sd;
-    const uint32_t gcol = static_cast<uint32_t>(m * a.B + bs);
-    if (a.layer == 0) {
-      int tok = a.tokens[static_cast<int64_t>(bs) * (a.T + 1) + a.t];
-      tok = min(max(tok, 0), a.V - 1);
-      xoff[k] = static_cast<uint32_t>((m * a.V + tok) * a.E + 8 * p);
-    } else {
-      xoff[k] = gcol * static_cast<uint32_t>(H) + 8 * p;
-    }
-    hoff[k] = gcol * static_cast<uint32_t>(H) + 8 * p;
-  }
+  // ---- activation operand of this wave: lane holds column 64 cq + 16 j + lane % 16 of model
+  // m_out, k piece lane / 16 (the MFMA B layout). Columns past the batch read the padding or the
+  // next model's columns (results unused). Element offsets are 32-bit: the host guarantees that
+  // the padded column count times max(in, H) fits.
+  const int kp = lane >> 4;
+  const uint32_t gcol0 = static_cast<uint32_t>(m_out * a.B + bcol0 + 64 * cq + (lane & 15));
+  const uint32_t xoff = gcol0 * static_cast<uint32_t>(a.in) + 8 * kp;
+  const uint32_t hoff = gcol0 * static_cast<uint32_t>(H) + 8 * kp;
 
   const int kx = a.in / kKChunk;
   const int kh = a.first ? 0 : H / kKChunk;
   const int nch = kx + kh;
 
-  uint4 wpr, wmr;  // weight candidates of row ra for the next chunk
-  PhiloxOut oa{0, 0, 0, 0};
-
-  auto issue_b = [&](int c, int stage) {
+  auto load_w = [&](int c, uint4& wp_out, uint4& wm_out, uint32_t& word_out) {
     const bool xpart = c < kx;
     const int cc = xpart ? c : c - kx;
-    uint16_t* base = Bs + stage * kBStageElems + (4 * wave) * 512;  // 512 bf16 = 1024 bytes per load
-    const uint16_t* src = xpart ? xbase : a.h_prev;
-    const uint32_t kofs = static_cast<uint32_t>(kKChunk * cc);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t off = (xpart ? xoff[k] : hoff[k]) + kofs;
-      __builtin_amdgcn_global_load_lds(src + off, (__attribute__((address_space(3))) void*)(base + k * 512), 16, 0, 0);
-    }
-  };
-  auto load_w = [&](int c, uint4& wp_out, uint4& wm_out) {
-    const bool xpart = c < kx;
-    const int cc = xpart ? c : c - kx;
-    const int ld = xpart ? a.in : H;
-    const uint16_t* wp = xpart ? a.wp_ih : a.wp_hh;
-    const uint16_t* wm = xpart ? a.wm_ih : a.wm_hh;
-    const uint32_t off = static_cast<uint32_t>(grow * ld + kKChunk * cc + 8 * q);
+    const uint16_t* wp = (xpart ? a.wp_ih : a.wp_hh) + kKChunk * cc;
+    const uint16_t* wm = (xpart ? a.wm_ih : a.wm_hh) + kKChunk * cc;
+    const uint32_t off = xpart ? woff_x : woff_h;
     wp_out = *reinterpret_cast<const uint4*>(wp + off);
     wm_out = *reinterpret_cast<const uint4*>(wm + off);
+    word_out = (xpart ? sgx : sgh)[cc];
   };
-  // Philox words of the 128-column blocks used by chunks cc..cc+15 of a tensor: each lane of a
-  // row's quad evaluates a different block (one call per lane per 16 chunks).
-  auto philox_w = [&](int c) {
-    const bool xpart = c < kx;
-    const int cc = xpart ? c : c - kx;
-    if ((cc & 15) == 0) {
-      const uint32_t tensor = xpart ? a.tensor_ih : a.tensor_hh;
-      oa = sign_block(seed, tensor, static_cast<uint32_t>(grow), static_cast<uint32_t>((cc >> 2) + q));
-    }
-  };
-  // Selects the probe's weights for row ra of chunk c and writes both models' tiles to LDS.
-  // The word of chunk c is word (cc & 3) of the block; the lanes keep their four words rotating by
-  // one position per chunk (reset by philox_w), so it is always .x - no data-dependent selects.
-  auto form_w = [&](int c, const uint4& wpv, const uint4& wmv, int stage) {
-    const bool xpart = c < kx;
-    const int cc = xpart ? c : c - kx;
-    const int owner = (lane & ~3) | ((cc >> 2) & 3);  // the quad lane holding this block
-    const uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(oa.x), owner));
-    oa = PhiloxOut{oa.y, oa.z, oa.w, oa.x};
+  // Selects the probe's weights for row ra of one chunk (candidates wpv, wmv and the row's sign
+  // word of that chunk) and writes both models' tiles to LDS stage `stage`.
+  auto form_w = [&](const uint4& wpv, const uint4& wmv, uint32_t word, int stage) {
     // Piece q covers columns 8q..8q+7 of the 32-column word: pairs 4q..4q+3, which read bits
     // 4q+p (even column) and 16+4q+p (odd column).
     const uint32_t t4 = word >> (4 * q);
@@ -226,9 +193,9 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
       plus[p] = (mk & mv[p]) | (~mk & pv[p]);   // sign -1: +eps model takes w - eps
       minus[p] = (mk & pv[p]) | (~mk & mv[p]);
     }
-    uint16_t* st = As + stage * kAStageElems;
-    *reinterpret_cast<uint4*>(st + (0 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(plus[0], plus[1], plus[2], plus[3]);
-    *reinterpret_cast<uint4*>(st + (1 * kTileRows + ra) * kAStride + 8 * q) = make_uint4(minus[0], minus[1], minus[2], minus[3]);
+    char* st = As + stage * kAStageBytes;
+    *reinterpret_cast<uint4*>(st + piece_offset(ra, q)) = make_uint4(plus[0], plus[1], plus[2], plus[3]);
+    *reinterpret_cast<uint4*>(st + piece_offset(kTileRows + ra, q)) = make_uint4(minus[0], minus[1], minus[2], minus[3]);
   };
 
   f32x4 acc[8][4];
@@ -236,77 +203,114 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto mma = [&](int astage, int bstage) {
-    const uint16_t* A = As + astage * kAStageElems + (side * kTileRows + (lane & 15)) * kAStride + 8 * (lane >> 4);
-    const char* Bb = reinterpret_cast<const char*>(Bs + bstage * kBStageElems);
-    bf16x8 afr[8], bfr[4];
+  // A fragments: row group i of a chunk lives in afr[i % 4] and is read from LDS two groups
+  // before it is multiplied (row groups 0-1 of the next chunk at the end of the current one).
+  bf16x8 afr[4];
+  bf16x8 bq[kBRing][4];
+  const int a_lane_off = piece_offset(side * kTileRows + (lane & 15), kp);
+  auto read_a = [&](int stage, int i, bf16x8& dst) {
+    // row group i: 16 * i rows further, i.e. 1024 * i bytes (the swizzle repeats every 16 rows)
+    dst = *reinterpret_cast<const bf16x8*>(As + stage * kAStageBytes + a_lane_off + 1024 * i);
+  };
+  auto mma_group = [&](int i, const bf16x8& af, const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[j], acc[i][j], 0, 0, 0);
+  };
+  // Activations of chunks c and c+1 (c even), fragment by fragment, so that the two 64-byte
+  // halves of every 128-byte line go out in consecutive loads and the L1 fetches the line once.
+  auto load_b_pair = [&](int c, bf16x8 (&d0)[4], bf16x8 (&d1)[4]) {
+    const int c0 = min(c, nch - 1), c1 = min(c + 1, nch - 1);
+    const bool x0p = c0 < kx, x1p = c1 < kx;
+    const uint16_t* s0 = (x0p ? a.x_in : a.h_prev) + kKChunk * (x0p ? c0 : c0 - kx);
+    const uint16_t* s1 = (x1p ? a.x_in : a.h_prev) + kKChunk * (x1p ? c1 : c1 - kx);
+    const int ld0 = x0p ? a.in : H, ld1 = x1p ? a.in : H;
+    const uint32_t o0 = x0p ? xoff : hoff, o1 = x1p ? xoff : hoff;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int cidx = 256 * side + 64 * cq + 16 * j + (lane & 15);
-      bfr[j] = *reinterpret_cast<const bf16x8*>(Bb + b_piece_offset(cidx, lane >> 4));
+      d0[j] = *reinterpret_cast<const bf16x8*>(s0 + 16 * j * ld0 + o0);
+      d1[j] = *reinterpret_cast<const bf16x8*>(s1 + 16 * j * ld1 + o1);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) afr[i] = *reinterpret_cast<const bf16x8*>(A + 16 * i * kAStride);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
-  // One K step: chunk c is multiplied (A stage c&1, B stage c%3) while the loads of chunk c+1's
-  // weights and chunk c+2's activations are in flight; then chunk c+1 is selected into A stage
-  // (c+1)&1. The issue sequence has no branches (past the last chunk it reloads the last chunk
-  // into a stage that is not read again, and the select writes an unused A stage), so at the
-  // wait exactly the 4 activation loads of step c may still be outstanding.
-  auto kstep = [&](int c) {
-    load_w(min(c + 1, nch - 1), wpr, wmr);
-    __builtin_amdgcn_sched_barrier(0);  // weights strictly before activations (wait accounting)
-    issue_b(min(c + 2, nch - 1), (c + 2) % kBStages);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    mma(c & 1, c % kBStages);
+  // One K step on chunk c (c % 4 == S). Requests go out at the top: first the weight candidates
+  // of chunk c+3, then (on even c) the activations of chunks c+2 and c+3. Vector loads complete
+  // in issue order, and each stream is consumed in issue order, so this order never makes a wait
+  // for one chunk hold up a newer chunk: the weights of chunk c+3 are waited for in step c+1,
+  // after everything issued before them was needed anyway. Row groups 0-3 are multiplied; chunk
+  // c+2 is selected into its stage; row groups 4-7 finish, the last two followed by the reads of
+  // row groups 0-1 of chunk c+1. Past the last chunk the requests repeat the last chunk and the
+  // select fills a stage that is never multiplied.
+  //
+  // One barrier per step, right after the select, orders the weight ring: the select of chunk
+  // c+2 overwrites the stage of chunk c-2, whose last reads (row groups 4-7 in step c-2, after
+  // that step's barrier) every wave retired before the barrier of step c-1; the fragments of
+  // chunk c+1 are first read after the barrier of step c-1, which follows their select.
+  uint4 wp_r[2], wm_r[2];  // weight candidate ring: chunk k in slot k % 2
+  uint32_t wd_r[2];
+  auto step = [&](int c, auto S) {
+    constexpr int s_ = decltype(S)::value;
+    constexpr int wuse = s_ % 2, wnew = (s_ + 1) % 2;
+    const int rs = c & (kAStages - 1), rs1 = (c + 1) & (kAStages - 1), ws = (c + 2) & (kAStages - 1);
+    load_w(min(c + 3, nch - 1), wp_r[wnew], wm_r[wnew], wd_r[wnew]);
+    if constexpr (s_ % 2 == 0) load_b_pair(c + 2, bq[(s_ + 2) % 4], bq[(s_ + 3) % 4]);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    philox_w(c + 1);
-    form_w(c + 1, wpr, wmr, (c + 1) & 1);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mma_group(i, afr[i % 4], bq[s_]);
+      if (i + 2 < 8) read_a(rs, i + 2, afr[(i + 2) % 4]);
+      else read_a(rs1, i - 6, afr[(i + 2) % 4]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 3) {
+        form_w(wp_r[wuse], wm_r[wuse], wd_r[wuse], ws);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   // Gate biases of both models for the tile's 32 units, [model][gate][unit], into LDS.
-  float* bias_s = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + kGateBiasOffset);
+  float* bias_s = reinterpret_cast<float*>(As + kGateBiasOffset);
   if (tid < 2 * 4 * kUnitsPerTile) {
     const int sd = tid >> 7, g = (tid >> 5) & 3, u = tid & 31;
     bias_s[tid] = a.bias_m[(static_cast<int64_t>(2 * pr + sd) * a.L + a.layer) * (4 * H) + g * H + u0 + u];
   }
-  // Cell state of this lane's 8 x 4 cells, loaded now so its latency hides under the K loop.
-  const int m_out = 2 * pr + side;
-  const uint32_t ncols = static_cast<uint32_t>(a.Ncols);
-  float cst[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = bcol0 + 64 * cq + 16 * j + (lane & 15);
-      const uint32_t coff = static_cast<uint32_t>(u0 + 4 * i + (lane >> 4)) * ncols +
-                            static_cast<uint32_t>(m_out * a.B + (b < a.B ? b : 0));
-      cst[i][j] = a.first ? 0.f : a.c[coff];
-    }
 
-  // Prologue: activations of chunks 0 and 1 in flight, chunk 0 selected into A stage 0.
-  issue_b(0, 0);
-  load_w(0, wpr, wmr);
-  if (nch > 1) {
-    issue_b(1, 1);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Prologue: activations of chunks 0 and 1 and weight candidates of chunks 0-2 requested,
+  // chunks 0 and 1 selected into stages 0 and 1, row groups 0-1 of chunk 0 read.
+  {
+    uint4 wp0, wm0, wp1, wm1;
+    uint32_t w0, w1;
+    load_w(0, wp0, wm0, w0);
+    load_w(min(1, nch - 1), wp1, wm1, w1);
+    load_w(min(2, nch - 1), wp_r[0], wm_r[0], wd_r[0]);
+    load_b_pair(0, bq[0], bq[1]);
+    form_w(wp0, wm0, w0, 0);
+    form_w(wp1, wm1, w1, 1);
   }
-  philox_w(0);
-  form_w(0, wpr, wmr, 0);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) kstep(c);
-  // The last steps leave activation loads in flight; LDS is reused below.
+  read_a(0, 0, afr[0]);
+  read_a(0, 1, afr[1]);
+
+  static_assert(kBRing == 4, "the step is unrolled for a ring of 4");
+  int c = 0;
+  for (; c + 4 <= nch; c += 4) {
+    step(c, std::integral_constant<int, 0>{});
+    step(c + 1, std::integral_constant<int, 1>{});
+    step(c + 2, std::integral_constant<int, 2>{});
+    step(c + 3, std::integral_constant<int, 3>{});
+  }
+  if (c < nch) step(c, std::integral_constant<int, 0>{});
+  if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>{});
+  if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>{});
+
+  // Cell state of this lane's 8 x 4 cells: tile-private, stored in accumulator order, so each
+  // row group is one 16-byte access per lane and 1 KB per wave.
+  const int64_t tile = (static_cast<int64_t>(pr) * a.n_col_blocks + cb) * a.n_row_tiles + rt;
+  float4* cptr = reinterpret_cast<float4*>(a.c_tile) + (tile * 8 + wave) * 8 * 64 + lane;
+  float4 cst[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cst[i] = a.first ? make_float4(0.f, 0.f, 0.f, 0.f) : cptr[64 * i];
+  // Requests past the last chunk may still be in flight; the weight ring is reused below.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -315,21 +319,18 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ul = 4 * i + (lane >> 4);
-    const int u = u0 + ul;
     const float* bs = bias_s + side * 4 * kUnitsPerTile + ul;
     const float bi = bs[0], bf = bs[kUnitsPerTile], bg = bs[2 * kUnitsPerTile], bo = bs[3 * kUnitsPerTile];
+    const float cprev[4] = {cst[i].x, cst[i].y, cst[i].z, cst[i].w};
+    float cn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cl = 64 * cq + 16 * j + (lane & 15);
-      const int b = bcol0 + cl;
-      if (b < a.B) {
-        const uint32_t coff = static_cast<uint32_t>(u) * ncols + static_cast<uint32_t>(m_out * a.B + b);
-        float cn, hv;
-        lstm_cell(acc[i][j][0] + bi, acc[i][j][1] + bf, acc[i][j][2] + bg, acc[i][j][3] + bo, cst[i][j], cn, hv);
-        a.c[coff] = cn;
-        Hs[(256 * side + cl) * kHsStride + ul] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
-      }
+      float hv;
+      lstm_cell(acc[i][j][0] + bi, acc[i][j][1] + bf, acc[i][j][2] + bg, acc[i][j][3] + bo, cprev[j], cn[j], hv);
+      Hs[(256 * side + cl) * kHsStride + ul] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
     }
+    cptr[64 * i] = make_float4(cn[0], cn[1], cn[2], cn[3]);
   }
   __syncthreads();
   {
