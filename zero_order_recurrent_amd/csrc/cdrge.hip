@@ -146,8 +146,7 @@ Plan make_plan(const cdrge_config* c) {
   p.n_tiles = int64_t(p.H / kUnitsPerTile) * ((p.B + kTileCols - 1) / kTileCols) * p.P;
   if (c->dtype == CDRGE_BF16) {
     for (const TensorDesc& t : p.tensors) {
-      const bool gemm = (t.id != 0) && (t.rows > 1);  // W_ih, W_hh, W_out
-      if (!gemm) continue;
+      if (t.id != static_cast<uint32_t>(1 + 3 * p.L)) continue;  // W_out: candidates for the logits kernel
       p.off_wp[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
       p.off_wm[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
     }
@@ -247,7 +246,7 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
   if (bf16) {
     const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
     for (const TensorDesc& t : p.tensors) {
-      if (t.id == 0 || t.rows == 1) continue;
+      if (t.id != static_cast<uint32_t>(1 + 3 * p.L)) continue;  // W_out only; the gate kernels form their own
       const int64_t n = t.rows * t.cols;
       CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
         hipLaunchKernelGGL(k_pm_table_bf16, dim3(static_cast<uint32_t>((n / 8 + 256) / 256)), dim3(256), 0, s,
@@ -336,10 +335,9 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           GateArgs g;
           const TensorDesc& tih = p.tensors[1 + 3 * l];
           const TensorDesc& thh = p.tensors[2 + 3 * l];
-          g.wp_ih = ctx->at<uint16_t>(p.off_wp[tih.id]);
-          g.wm_ih = ctx->at<uint16_t>(p.off_wm[tih.id]);
-          g.wp_hh = ctx->at<uint16_t>(p.off_wp[thh.id]);
-          g.wm_hh = ctx->at<uint16_t>(p.off_wm[thh.id]);
+          g.w_ih = theta + tih.off;
+          g.w_hh = theta + thh.off;
+          g.eps = eps;
           g.sg_ih = ctx->at<uint32_t>(p.off_sg[tih.id]);
           g.sg_hh = ctx->at<uint32_t>(p.off_sg[thh.id]);
           g.x_in = (l == 0) ? x0 : hbuf(l - 1, t & 1);

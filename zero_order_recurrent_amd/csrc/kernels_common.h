@@ -78,27 +78,28 @@ __global__ void k_pm_table_bf16(const uint16_t* __restrict__ w, int64_t n, float
 }
 
 // The probe sign bits of one recurrent weight tensor [rows][cols] (cols a multiple of 32) for
-// the probe pairs pair0 .. pair0 + pc - 1 of a chunk, as 32-bit words in column order:
-// out[q][r][w] covers columns 32w .. 32w + 31 of row r and is word (w & 3) of the Philox block
+// the probe pairs pair0 .. pair0 + pc - 1 of a chunk, as 32-bit words stored chunk-major:
+// out[q][w][r] covers columns 32w .. 32w + 31 of row r and is word (w & 3) of the Philox block
 // w >> 2, so bit ((c & 31) >> 1) | ((c & 1) << 4) of word c >> 5 is the sign bit of column c.
-// The gate kernels read one word per row and 32-column chunk instead of regenerating the same
-// Philox blocks for every timestep and column tile. One thread per (pair, row, 128-column block).
+// The gate kernels read the words of one 32-column chunk for runs of consecutive rows (whole
+// cache lines) instead of regenerating the same Philox blocks for every timestep and column
+// tile. One thread per (pair, 128-column block, row), rows fastest so that stores coalesce.
 __global__ void k_sign_words(const uint64_t* __restrict__ seeds, int pair0, int pc, uint32_t tensor,
                              int rows, int wpr, uint32_t* __restrict__ out) {
   const int nblk = (wpr + 3) / 4;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(pc) * rows * nblk) return;
-  const int blk = static_cast<int>(i % nblk);
-  const int64_t qr = i / nblk;
-  const int r = static_cast<int>(qr % rows);
-  const int q = static_cast<int>(qr / rows);
+  const int r = static_cast<int>(i % rows);
+  const int64_t qb = i / rows;
+  const int blk = static_cast<int>(qb % nblk);
+  const int q = static_cast<int>(qb / nblk);
   const PhiloxOut o = sign_block(seeds[pair0 + q], tensor, static_cast<uint32_t>(r), static_cast<uint32_t>(blk));
-  uint32_t* dst = out + qr * wpr + 4 * blk;
-  const int nw = min(4, wpr - 4 * blk);
   const uint32_t w[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (k < nw) dst[k] = w[k];
+  for (int k = 0; k < 4; ++k) {
+    const int wi = 4 * blk + k;
+    if (wi < wpr) out[(static_cast<int64_t>(q) * wpr + wi) * rows + r] = w[k];
+  }
 }
 
 // Per-model perturbed copy of a small tensor [rows][cols] of a bf16 model, for models

@@ -40,6 +40,8 @@ namespace cdrge {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGateThreads = 512;
 constexpr int kUnitsPerTile = 32;
@@ -93,17 +95,16 @@ __device__ __forceinline__ void lstm_cell(float gi, float gf, float gg, float go
 __device__ __forceinline__ int piece_offset(int r, int p) { return r * 64 + 16 * (p ^ ((r >> 2) & 3)); }
 
 struct GateArgs {
-  const uint16_t* wp_ih;
-  const uint16_t* wm_ih;   // [4H][in] candidates of W_ih
-  const uint16_t* wp_hh;
-  const uint16_t* wm_hh;   // [4H][H] candidates of W_hh
-  const uint32_t* sg_ih;   // sign words of W_ih for the chunk's pairs, [pairs][4H][in / 32]
-  const uint32_t* sg_hh;   // sign words of W_hh, [pairs][4H][H / 32]
+  const uint16_t* w_ih;    // W_ih [4H][in], bf16 parameters
+  const uint16_t* w_hh;    // W_hh [4H][H]
+  const uint32_t* sg_ih;   // sign words of W_ih for the chunk's pairs, [pairs][in / 32][4H]
+  const uint32_t* sg_hh;   // sign words of W_hh, [pairs][H / 32][4H]
   const uint16_t* x_in;    // input of this layer at t, [columns][in] (padded columns readable)
   const uint16_t* h_prev;  // this layer's h_{t-1}, [columns][H] (unused when first)
   uint16_t* h_out;         // this layer's h_t, [columns][H]
   float* c_tile;           // this layer's cell state in accumulator order, 64 KB per tile
   const float* bias_m;     // per-model perturbed gate bias [2P][L][4H]
+  float eps;
   int in, H, B, L, layer, first;
   int n_row_tiles, n_col_blocks, n_pairs, swizzle;
 };
@@ -151,9 +152,10 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   const int grow = (ra & 3) * H + u0 + (ra >> 2);
   const uint32_t woff_x = static_cast<uint32_t>(grow * a.in + 8 * q);
   const uint32_t woff_h = static_cast<uint32_t>(grow * H + 8 * q);
-  // sign words of row grow for this pair: one 32-bit word per 32-column chunk
-  const uint32_t* sgx = a.sg_ih + (static_cast<int64_t>(pr) * 4 * H + grow) * (a.in / kKChunk);
-  const uint32_t* sgh = a.sg_hh + (static_cast<int64_t>(pr) * 4 * H + grow) * (H / kKChunk);
+  // sign words of row grow for this pair: one 32-bit word per 32-column chunk, chunk-major, so
+  // the 128 rows of a tile read 4 runs of 32 consecutive words per chunk
+  const uint32_t* sgx = a.sg_ih + static_cast<int64_t>(pr) * (a.in / kKChunk) * (4 * H) + grow;
+  const uint32_t* sgh = a.sg_hh + static_cast<int64_t>(pr) * (H / kKChunk) * (4 * H) + grow;
 
   // ---- activation operand of this wave: lane holds column 64 cq + 16 j + lane % 16 of model
   // m_out, k piece lane / 16 (the MFMA B layout). Columns past the batch read the padding or the
@@ -168,30 +170,34 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   const int kh = a.first ? 0 : H / kKChunk;
   const int nch = kx + kh;
 
-  auto load_w = [&](int c, uint4& wp_out, uint4& wm_out, uint32_t& word_out) {
+  auto load_w = [&](int c, uint4& w_out, uint32_t& word_out) {
     const bool xpart = c < kx;
     const int cc = xpart ? c : c - kx;
-    const uint16_t* wp = (xpart ? a.wp_ih : a.wp_hh) + kKChunk * cc;
-    const uint16_t* wm = (xpart ? a.wm_ih : a.wm_hh) + kKChunk * cc;
-    const uint32_t off = xpart ? woff_x : woff_h;
-    wp_out = *reinterpret_cast<const uint4*>(wp + off);
-    wm_out = *reinterpret_cast<const uint4*>(wm + off);
-    word_out = (xpart ? sgx : sgh)[cc];
+    const uint16_t* w = (xpart ? a.w_ih : a.w_hh) + kKChunk * cc;
+    w_out = *reinterpret_cast<const uint4*>(w + (xpart ? woff_x : woff_h));
+    word_out = (xpart ? sgx : sgh)[static_cast<int64_t>(cc) * (4 * H)];
   };
-  // Selects the probe's weights for row ra of one chunk (candidates wpv, wmv and the row's sign
-  // word of that chunk) and writes both models' tiles to LDS stage `stage`.
-  auto form_w = [&](const uint4& wpv, const uint4& wmv, uint32_t word, int stage) {
+  // Selects the probe's weights for row ra of one chunk (8 bf16 weights wv and the row's sign
+  // word of that chunk) and writes both models' tiles to LDS stage `stage`. The two candidates
+  // bf16(w + eps) and bf16(w - eps) are formed here (one float add each, then the packed
+  // round-to-nearest-even conversion) and the sign bit picks one per model.
+  const float eps = a.eps;
+  auto form_w = [&](const uint4& wv, uint32_t word, int stage) {
     // Piece q covers columns 8q..8q+7 of the 32-column word: pairs 4q..4q+3, which read bits
     // 4q+p (even column) and 16+4q+p (odd column).
     const uint32_t t4 = word >> (4 * q);
-    const uint32_t pv[4] = {wpv.x, wpv.y, wpv.z, wpv.w}, mv[4] = {wmv.x, wmv.y, wmv.z, wmv.w};
+    const uint32_t w2[4] = {wv.x, wv.y, wv.z, wv.w};
     uint32_t plus[4], minus[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+      const float lo = __uint_as_float(w2[p] << 16), hi = __uint_as_float(w2[p] & 0xffff0000u);
+      const f32x2 vp = {lo + eps, hi + eps}, vm = {lo - eps, hi - eps};
+      const uint32_t pv = __builtin_bit_cast(uint32_t, __builtin_convertvector(vp, bf16x2));
+      const uint32_t mv = __builtin_bit_cast(uint32_t, __builtin_convertvector(vm, bf16x2));
       // bits p and p+16 moved to 15 and 31, then replicated over each half-word
       const uint32_t mk = __builtin_amdgcn_perm(0u, t4 << (15 - p), 0x09090808u);
-      plus[p] = (mk & mv[p]) | (~mk & pv[p]);   // sign -1: +eps model takes w - eps
-      minus[p] = (mk & pv[p]) | (~mk & mv[p]);
+      plus[p] = (mk & mv) | (~mk & pv);   // sign -1: +eps model takes w - eps
+      minus[p] = (mk & pv) | (~mk & mv);
     }
     char* st = As + stage * kAStageBytes;
     *reinterpret_cast<uint4*>(st + piece_offset(ra, q)) = make_uint4(plus[0], plus[1], plus[2], plus[3]);
@@ -245,13 +251,13 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // c+2 overwrites the stage of chunk c-2, whose last reads (row groups 4-7 in step c-2, after
   // that step's barrier) every wave retired before the barrier of step c-1; the fragments of
   // chunk c+1 are first read after the barrier of step c-1, which follows their select.
-  uint4 wp_r[2], wm_r[2];  // weight candidate ring: chunk k in slot k % 2
+  uint4 w_r[2];  // weight ring: chunk k in slot k % 2
   uint32_t wd_r[2];
   auto step = [&](int c, auto S) {
     constexpr int s_ = decltype(S)::value;
     constexpr int wuse = s_ % 2, wnew = (s_ + 1) % 2;
     const int rs = c & (kAStages - 1), rs1 = (c + 1) & (kAStages - 1), ws = (c + 2) & (kAStages - 1);
-    load_w(min(c + 3, nch - 1), wp_r[wnew], wm_r[wnew], wd_r[wnew]);
+    load_w(min(c + 3, nch - 1), w_r[wnew], wd_r[wnew]);
     if constexpr (s_ % 2 == 0) load_b_pair(c + 2, bq[(s_ + 2) % 4], bq[(s_ + 3) % 4]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
       else read_a(rs1, i - 6, afr[(i + 2) % 4]);
       __builtin_amdgcn_sched_barrier(0);
       if (i == 3) {
-        form_w(wp_r[wuse], wm_r[wuse], wd_r[wuse], ws);
+        form_w(w_r[wuse], wd_r[wuse], ws);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -278,14 +284,14 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // Prologue: activations of chunks 0 and 1 and weight candidates of chunks 0-2 requested,
   // chunks 0 and 1 selected into stages 0 and 1, row groups 0-1 of chunk 0 read.
   {
-    uint4 wp0, wm0, wp1, wm1;
-    uint32_t w0, w1;
-    load_w(0, wp0, wm0, w0);
-    load_w(min(1, nch - 1), wp1, wm1, w1);
-    load_w(min(2, nch - 1), wp_r[0], wm_r[0], wd_r[0]);
+    uint4 w0, w1;
+    uint32_t d0, d1;
+    load_w(0, w0, d0);
+    load_w(min(1, nch - 1), w1, d1);
+    load_w(min(2, nch - 1), w_r[0], wd_r[0]);
     load_b_pair(0, bq[0], bq[1]);
-    form_w(wp0, wm0, w0, 0);
-    form_w(wp1, wm1, w1, 1);
+    form_w(w0, d0, 0);
+    form_w(w1, d1, 1);
   }
   __syncthreads();
   read_a(0, 0, afr[0]);
