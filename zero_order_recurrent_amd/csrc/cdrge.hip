@@ -15,6 +15,7 @@
 #include "kernels_common.h"
 #include "kernels_f32.h"
 #include "kernels_gates_bf16.h"
+#include "kernels_update.h"
 #include "philox.h"
 
 using namespace cdrge;
@@ -396,6 +397,27 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
                                         (2.0 * p.K * static_cast<double>(p.cfg.eps)));
   const bool bf16 = p.cfg.dtype == CDRGE_BF16;
   const size_t esz = bf16 ? 2 : 4;
+  if (bf16 && p.K <= kUpdLutMaxProbes && static_cast<int>(p.tensors.size()) <= kUpdMaxTensors) {
+    // all tensors in one launch (tensor ids are their positions in the flat layout)
+    UpdTensors ut{};
+    int64_t segs = 0;
+    ut.n = static_cast<int>(p.tensors.size());
+    for (int i = 0; i < ut.n; ++i) {
+      const TensorDesc& t = p.tensors[i];
+      segs += t.rows * ((t.cols + 127) / 128);
+      ut.seg_end[i] = segs;
+      ut.off[i] = t.off;
+      ut.rows[i] = static_cast<int>(t.rows);
+      ut.cols[i] = static_cast<int>(t.cols);
+    }
+    const int64_t blocks = (segs + kUpdLutThreads / 4 - 1) / (kUpdLutThreads / 4);
+    const dim3 lgrid(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096));
+    const double bytes = 2.0 * double(p.d) * 2;
+    return timed(ctx, 2, bytes, [&] {
+      hipLaunchKernelGGL(k_update_lut_bf16, lgrid, dim3(kUpdLutThreads), update_lut_bytes(p.K), s,
+                         static_cast<uint16_t*>(ctx->params), ut, seeds, losses, p.K, coef, flags);
+    });
+  }
   for (const TensorDesc& t : p.tensors) {
     const int64_t segs = t.rows * ((t.cols + 127) / 128);
     const dim3 grid(static_cast<uint32_t>((segs + 15) / 16));
@@ -418,6 +440,9 @@ cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   if (cfg->dtype == CDRGE_BF16) {
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_gates_bf16),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
+    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_update_lut_bf16),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(update_lut_bytes(kUpdLutMaxProbes))));
   } else {
     const int lds = static_cast<int>(sizeof(float) * f32_lds_floats(cfg->n_layers, cfg->vocab, cfg->embed,
                                                                     cfg->hidden, cfg->batch));

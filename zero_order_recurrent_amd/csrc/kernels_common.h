@@ -15,8 +15,9 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_fl
 // propagates into the exponent, so values past the largest bf16 become infinity.)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const bool nan = (u & 0x7fffffffu) > 0x7f800000u;
+  return nan ? ((u >> 16) | 0x40u) : rounded;  // a select, not a branch
 }
 
 // A perturbed weight: w + s*eps with s in {+1,-1}, in the model's storage precision.

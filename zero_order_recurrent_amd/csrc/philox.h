@@ -19,29 +19,31 @@ struct PhiloxOut {
 
 #define CDRGE_HD __host__ __device__ __forceinline__
 
-CDRGE_HD uint32_t mul_hi32(uint32_t a, uint32_t b) {
+// a ^ b ^ c; one three-input bit operation (truth table 0x96) on the device.
+CDRGE_HD uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  return __umulhi(a, b);
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 #else
-  return static_cast<uint32_t>((static_cast<uint64_t>(a) * b) >> 32);
+  return a ^ b ^ c;
 #endif
 }
 
-// Ten rounds; round r uses the key advanced r times by the Weyl constants.
+// Ten rounds; round r uses the key advanced r times by the Weyl constants. The 32 x 32 -> 64-bit
+// products give both halves at once (one v_mad_u64_u32 each on the device).
 CDRGE_HD PhiloxOut philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                             uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0;
-    const uint32_t hi0 = mul_hi32(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2;
-    const uint32_t hi1 = mul_hi32(0xCD9E8D57u, c2);
-    const uint32_t n0 = hi1 ^ c1 ^ k0;
-    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k1);
     c0 = n0;
-    c1 = lo1;
+    c1 = static_cast<uint32_t>(p1);
     c2 = n2;
-    c3 = lo0;
+    c3 = static_cast<uint32_t>(p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
