@@ -41,10 +41,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per gate-kernel launch from the committed counter summary, if it was taken on
-    the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"gates_bf16_{workload}_traffic.json")
+def traffic_from_profiles(kernel_tag: str, workload: str):
+    """HBM bytes per launch of a kernel from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy of known size), if it was taken on the current kernel
+    sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -60,14 +61,17 @@ def cpu_baseline(preset, theta, tokens, budget_s: float):
     o = Oracle()
     oc = OracleConfig(preset.n_layers, preset.vocab, preset.embed, preset.hidden, preset.batch,
                       preset.seq_len, preset.n_probes, preset.dtype, preset.eps, preset.lr, preset.base_seed)
-    n_seq = 1
-    t0 = time.perf_counter()
-    o.probe_losses(oc, theta, tokens, 0, probe_ids=[0], seq_ids=list(range(n_seq)))
-    one = time.perf_counter() - t0
-    n_seq = int(max(1, min(preset.batch, budget_s / max(one, 1e-3))))
-    t0 = time.perf_counter()
-    o.probe_losses(oc, theta, tokens, 0, probe_ids=[0], seq_ids=list(range(n_seq)))
-    dt = time.perf_counter() - t0
+    # the call's cost is a fixed part (the perturbed parameter copies) plus a per-sequence part
+    def timed(n):
+        t0 = time.perf_counter()
+        o.probe_losses(oc, theta, tokens, 0, probe_ids=[0], seq_ids=list(range(n)))
+        return time.perf_counter() - t0
+    n_probe = min(4, preset.batch)
+    t1, tn = timed(1), timed(n_probe)
+    per_seq = max((tn - t1) / max(n_probe - 1, 1), 1e-4)
+    fixed = max(t1 - per_seq, 0.0)
+    n_seq = int(max(1, min(preset.batch, (budget_s - fixed) / per_seq)))
+    dt = timed(n_seq)
     toks = 2 * n_seq * preset.seq_len
     return {"value": toks / dt, "unit": "perturbed-forward tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"probe pair 0 (both signs) x {n_seq} sequences x T={preset.seq_len} at full model "
@@ -81,8 +85,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="charlm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = 1 << 28  # float32 elements: 1 GiB per direction
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_direction": n * 4, "copies": 3}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (probe sharding across GPUs "
               "is a design note only). Run with --gpus 1.", file=sys.stderr)
@@ -140,7 +156,8 @@ def main():
     gate_mean_s = gate_ms / 1e3 / max(gate_n, 1)
     achieved = gate_flops_per_launch / gate_mean_s / 1e12 if gate_n else 0.0
     peak = PEAK["bf16_mfma_tflops"] if p.dtype == "bf16" else PEAK["fp32_tflops"]
-    traffic = traffic_from_profiles(args.workload)
+    traffic = traffic_from_profiles("gates_bf16" if p.dtype == "bf16" else "lstm_f32", args.workload)
+    upd_traffic = traffic_from_profiles("update_bf16" if p.dtype == "bf16" else "update_f32", args.workload)
     upd_ms, upd_n = timing[2]
     upd_gbs = work[2] / (upd_ms / 1e3) / 1e9 if upd_n else 0.0
     ce_ms, ce_n = timing[1]
@@ -169,7 +186,7 @@ def main():
                      "traffic": traffic, "launches": gate_n, "mean_launch_ms": gate_mean_s * 1e3,
                      "flops_per_launch": gate_flops_per_launch},
         "update_roofline": {"bound": "hbm", "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
-                            "frac": upd_gbs / PEAK["hbm_gbs"], "launches": upd_n,
+                            "frac": upd_gbs / PEAK["hbm_gbs"], "traffic": upd_traffic, "launches": upd_n,
                             "total_ms_per_step": upd_ms / args.steps},
         "time_split_ms_per_step": {"gates": gate_ms / args.steps, "logits_ce": ce_ms / args.steps,
                                    "update": upd_ms / args.steps, "prep": timing[3][0] / args.steps},
