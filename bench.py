@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -31,13 +32,21 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_tflops": 157.3, "hbm_gbs": 8000.0}
 
 
+def _code_tokens(text: str) -> bytes:
+    """Source text without comments and whitespace runs, so that editing a comment does not
+    make a profile of unchanged code look stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "zero_order_recurrent_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_tokens(f.read()))
     return h.hexdigest()[:16]
 
 

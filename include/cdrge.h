@@ -89,7 +89,8 @@ int64_t cdrge_param_count(const cdrge_config* cfg);
 /* CDRGE_OK if the configuration is valid and supported; otherwise the reason.
  * Supported: F32 whenever one probe pair's recurrent state fits the on-chip buffers
  * (about 2 * B * (2 L H + 4 H + max(E, H)) floats <= 48K); BF16 when E % 32 == 0,
- * H % 32 == 0 and V <= 64. */
+ * H % 32 == 0, V <= 64, and one probe chunk's activations stay within 32-bit element offsets:
+ * (2 * probes_per_chunk * B + 256) * max(E, H) < 2^31 and 4 H max(E, H) < 2^31. */
 cdrge_status cdrge_check_config(const cdrge_config* cfg);
 
 /* Device workspace, in bytes, that cdrge_init needs for this configuration (256-byte aligned

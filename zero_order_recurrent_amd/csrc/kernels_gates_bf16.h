@@ -7,10 +7,13 @@
 // perturbed weights that the method evaluates (alex-wiki source note on arXiv 2505.17852,
 // "Method"), with Rademacher perturbations (pith.science review, "What carries the argument").
 //
-// The perturbed weight tile is never stored to memory: per step the probe-independent candidates
-// Wp = bf16(W + eps) and Wm = bf16(W - eps) exist once in memory, and each probe's tile is a
-// per-element bit select between them, driven by the probe's Philox sign bits, done in registers
-// on the way into LDS. Both models of a pair share the loaded candidates and the sign bits.
+// The perturbed weight tile is never stored to memory. Each thread loads 8 stored weights w of
+// one row, forms both candidates bf16(w + eps) and bf16(w - eps) in registers (one float add each
+// and the packed round-to-nearest-even conversion), and the probe's sign bit picks one candidate
+// per model: the +eps model takes the one the sign selects, the -eps model the other. The result
+// goes to LDS. Sign bits come from per-step tables of Philox words (one 32-bit word per row and
+// 32-column chunk, chunk-major), so both models of a pair share one weight load and one sign
+// word.
 //
 // Workgroup tile (512 threads = 8 waves of 64 lanes, two per SIMD):
 //   rows    128 gate rows = 32 hidden units x 4 gates, interleaved (local row 4u + g is gate g of
@@ -20,12 +23,14 @@
 //           (128 accumulator registers per lane).
 // K loop over the concatenated reduction [x_t ; h_{t-1}] in chunks of 32, software-pipelined:
 //   * activations go straight from global memory into the MFMA operand registers of the wave
-//     that uses them (each column belongs to one wave), two chunks ahead, in a 3-deep ring;
-//   * the selected weight tiles of both models live in a 3-stage LDS ring. While chunk c is
-//     multiplied, every wave reads its fragments of chunk c+1 (row group i right after the MFMAs
-//     that last use row group i of chunk c), and the workgroup selects chunk c+2 into the third
-//     stage; one barrier per chunk, placed right after that select, orders it all;
-//   * the weight candidates of chunk c+2 are loaded coalesced one chunk before they are selected.
+//     that uses them (each column belongs to one wave), in a 4-deep register ring, two chunks at
+//     a time so that both 64-byte halves of a 128-byte line are requested back to back;
+//   * the stored weights and sign words of chunk c+3 are requested at the top of step c into a
+//     2-slot register ring, and selected into LDS in step c+1;
+//   * the selected tiles of both models live in a 4-stage LDS ring; fragments are read two row
+//     groups ahead of the MFMAs that use them; one barrier per chunk, right after the select.
+// The cell state stays in accumulator order (tile-private, 16 bytes per lane and row group), and
+// h leaves through an LDS transpose as whole 64-byte column segments.
 // The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 8 row
 // tiles x 4 column blocks, which keeps their shared weight and activation chunks in that XCD's L2.
 #pragma once
