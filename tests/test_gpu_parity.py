@@ -2,7 +2,8 @@
 
 Shapes span several tiles and ragged tails: bf16 batches that are not a multiple of the 128-column
 tile, several 64-unit row tiles, two layers, probe chunks of unequal size; fp32 batches split over
-two workgroups. Bars: probe seeds and signs bit-exact; losses and per-sequence losses within
+two workgroups, two probe pairs per workgroup with an odd pair count, more gate rows than threads,
+inputs that are not a multiple of 32 columns. Bars: probe seeds and signs bit-exact; losses and per-sequence losses within
 1e-5 (fp32) or 2e-2 (bf16) relative; updated parameters within the same bars normwise per tensor.
 """
 import numpy as np
@@ -17,6 +18,11 @@ pytestmark = pytest.mark.gpu
 SMALL = {
     "f32_ragged": b.make_config(2, 13, 20, 24, 11, 5, 3, "f32", 1e-3, 1e-3, 77, probes_per_chunk=2),
     "f32_long": b.make_config(1, 32, 16, 40, 2, 40, 4, "f32", 1e-3, 1e-3, 78),
+    # 515 pairs: two pairs per workgroup, the last workgroup with one; 3 sequences over two
+    # workgroups of two slots
+    "f32_pairs2": b.make_config(1, 7, 12, 8, 3, 4, 515, "f32", 1e-3, 1e-3, 82),
+    # 4H = 1,280 rows over 1,024 threads: rows wrap; V = 70 logit rows over 14 column slices
+    "f32_wide": b.make_config(1, 70, 40, 320, 1, 3, 2, "f32", 1e-3, 1e-3, 83),
     "bf16_ragged": b.make_config(2, 50, 64, 128, 160, 3, 3, "bf16", 1e-4, 1e-4, 79, probes_per_chunk=2),
     "bf16_e32_v5": b.make_config(1, 5, 32, 64, 40, 4, 2, "bf16", 1e-2, 1e-2, 80),
     "bf16_v64": b.make_config(3, 64, 96, 192, 130, 2, 2, "bf16", 1e-3, 1e-3, 81),

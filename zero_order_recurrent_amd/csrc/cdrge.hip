@@ -24,8 +24,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxProbes = 1024;
-constexpr int kMaxF32Layers = 8;
-constexpr int64_t kMaxF32LdsBytes = 64 * 1024;
+constexpr int64_t kMaxF32LdsBytes = 128 * 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -57,7 +56,9 @@ struct Plan {
   size_t off_flags, off_seeds, off_seq, off_emb_m, off_bias_m, off_bout_m, off_x0, off_h, off_c, total;
   int64_t ncols_pad, n_tiles;  // bf16: padded column count of the activation buffers; gate tiles per chunk
   std::vector<size_t> off_wp, off_wm;  // per tensor id (bf16 matrices only)
-  std::vector<size_t> off_sg;          // per tensor id (bf16 W_ih, W_hh): sign words of a chunk
+  std::vector<size_t> off_sg;          // per tensor id (W_ih, W_hh; fp32 also W_out): sign words of a chunk
+  std::vector<size_t> off_wt;          // per tensor id (fp32 W_ih, W_hh, W_out): k-major copy W^T
+  int f32_g, f32_nb, f32_threads;      // fp32: pairs and sequences per workgroup, threads
 };
 
 bool basic_valid(const cdrge_config* c) {
@@ -82,16 +83,20 @@ cdrge_status supported(const cdrge_config* c) {
   const int64_t d = param_count(c);
   if (d >= (int64_t(1) << 40)) return CDRGE_ERR_UNSUPPORTED;
   if (int64_t(c->batch) * (c->seq_len + 1) >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
+  const int P = (c->probes_per_chunk == 0 || c->probes_per_chunk > c->n_probes) ? c->n_probes
+                                                                               : c->probes_per_chunk;
   if (c->dtype == CDRGE_F32) {
-    if (c->n_layers > kMaxF32Layers) return CDRGE_ERR_UNSUPPORTED;
-    if (int64_t(4) * f32_lds_floats(c->n_layers, c->vocab, c->embed, c->hidden, c->batch) > kMaxF32LdsBytes)
-      return CDRGE_ERR_UNSUPPORTED;
-    if (int64_t(4) * c->hidden >= (int64_t(1) << 30)) return CDRGE_ERR_UNSUPPORTED;
+    if (c->n_layers > kF32MaxLayers) return CDRGE_ERR_UNSUPPORTED;
+    if (c->hidden > (1 << 16) || c->embed > (1 << 16) || c->vocab > (1 << 16)) return CDRGE_ERR_UNSUPPORTED;
+    const int nb = f32_nb(c->batch);
+    const F32Lds lay = f32_lds_layout(c->n_layers, c->vocab, c->embed, c->hidden, f32_g(nb, P), nb,
+                                      f32_threads(c->hidden));
+    if (int64_t(4) * lay.total > kMaxF32LdsBytes) return CDRGE_ERR_UNSUPPORTED;
+    const int64_t maxdim = c->embed > c->hidden ? c->embed : c->hidden;
+    if (int64_t(4) * c->hidden * maxdim >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
   } else {
     if (c->embed % 32 != 0 || c->hidden % kUnitsPerTile != 0 || c->vocab > kCeRows)
       return CDRGE_ERR_UNSUPPORTED;
-    const int P = (c->probes_per_chunk == 0 || c->probes_per_chunk > c->n_probes) ? c->n_probes
-                                                                                 : c->probes_per_chunk;
     const int64_t maxdim = c->embed > c->hidden ? c->embed : c->hidden;
     if ((int64_t(2) * P * c->batch + kTileCols) * maxdim >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
     if (int64_t(2) * P * c->vocab * c->embed >= (int64_t(1) << 31)) return CDRGE_ERR_UNSUPPORTED;
@@ -142,6 +147,10 @@ Plan make_plan(const cdrge_config* c) {
   p.off_wp.assign(p.tensors.size(), 0);
   p.off_wm.assign(p.tensors.size(), 0);
   p.off_sg.assign(p.tensors.size(), 0);
+  p.off_wt.assign(p.tensors.size(), 0);
+  p.f32_nb = f32_nb(p.B);
+  p.f32_g = f32_g(p.f32_nb, p.P);
+  p.f32_threads = f32_threads(p.H);
   p.off_emb_m = p.off_bias_m = p.off_bout_m = p.off_x0 = p.off_h = p.off_c = 0;
   p.ncols_pad = ncols + kTileCols;
   p.n_tiles = int64_t(p.H / kUnitsPerTile) * ((p.B + kTileCols - 1) / kTileCols) * p.P;
@@ -160,6 +169,16 @@ Plan make_plan(const cdrge_config* c) {
     p.off_x0 = region(sizeof(uint16_t) * p.ncols_pad * p.E);
     p.off_h = region(sizeof(uint16_t) * int64_t(p.L) * 2 * p.ncols_pad * p.H);
     p.off_c = region(sizeof(float) * int64_t(p.L) * p.n_tiles * kGateThreads * 32);
+  } else {
+    for (int l = 0; l <= p.L; ++l) {
+      const std::initializer_list<TensorDesc> mats =
+          (l < p.L) ? std::initializer_list<TensorDesc>{p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]}
+                    : std::initializer_list<TensorDesc>{p.tensors[1 + 3 * p.L]};
+      for (const TensorDesc& t : mats) {
+        p.off_wt[t.id] = region(sizeof(float) * t.rows * t.cols);
+        p.off_sg[t.id] = region(sizeof(uint32_t) * p.P * t.rows * ((t.cols + 31) / 32));
+      }
+    }
   }
   p.total = w;
   return p;
@@ -244,6 +263,17 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
   }));
 
   const bool bf16 = p.cfg.dtype == CDRGE_BF16;
+  if (!bf16) {
+    const float* theta = static_cast<const float*>(ctx->params);
+    for (const TensorDesc& t : p.tensors) {
+      if (p.off_wt[t.id] == 0) continue;  // not a matrix of the fp32 path (offset 0 holds the flags)
+      const dim3 grid(static_cast<uint32_t>((t.cols + 31) / 32), static_cast<uint32_t>((t.rows + 31) / 32));
+      CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+        hipLaunchKernelGGL(k_transpose_f32, grid, dim3(256), 0, s, theta + t.off, static_cast<int>(t.rows),
+                           static_cast<int>(t.cols), ctx->at<float>(p.off_wt[t.id]));
+      }));
+    }
+  }
   if (bf16) {
     const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
     for (const TensorDesc& t : p.tensors) {
@@ -262,26 +292,52 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
     const int models = 2 * pc;
     const int ncols = models * p.B;
     if (!bf16) {
-      F32Model m;
+      for (int l = 0; l <= p.L; ++l) {
+        const std::initializer_list<TensorDesc> mats =
+            (l < p.L) ? std::initializer_list<TensorDesc>{p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]}
+                      : std::initializer_list<TensorDesc>{p.tensors[1 + 3 * p.L]};
+        for (const TensorDesc& t : mats) {
+          const int wpr = static_cast<int>((t.cols + 31) / 32);
+          const int64_t n = int64_t(pc) * t.rows * ((wpr + 3) / 4);
+          CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+            hipLaunchKernelGGL(k_sign_words, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, seeds,
+                               pair0, pc, t.id, static_cast<int>(t.rows), wpr, ctx->at<uint32_t>(p.off_sg[t.id]));
+          }));
+        }
+      }
+      F32Args m;
       m.theta = static_cast<const float*>(ctx->params);
       m.off_emb = p.tensors[0].off;
-      for (int l = 0; l < p.L; ++l) {
-        m.off_wih[l] = p.tensors[1 + 3 * l].off;
-        m.off_whh[l] = p.tensors[2 + 3 * l].off;
-        m.off_b[l] = p.tensors[3 + 3 * l].off;
-      }
-      m.off_wout = p.tensors[1 + 3 * p.L].off;
       m.off_bout = p.tensors[2 + 3 * p.L].off;
+      for (int l = 0; l < kF32MaxLayers; ++l) {
+        const bool on = l < p.L;
+        m.off_b[l] = on ? p.tensors[3 + 3 * l].off : 0;
+        m.wt_ih[l] = on ? ctx->at<float>(p.off_wt[1 + 3 * l]) : nullptr;
+        m.wt_hh[l] = on ? ctx->at<float>(p.off_wt[2 + 3 * l]) : nullptr;
+        m.sg_ih[l] = on ? ctx->at<uint32_t>(p.off_sg[1 + 3 * l]) : nullptr;
+        m.sg_hh[l] = on ? ctx->at<uint32_t>(p.off_sg[2 + 3 * l]) : nullptr;
+      }
+      m.wt_out = ctx->at<float>(p.off_wt[1 + 3 * p.L]);
+      m.sg_out = ctx->at<uint32_t>(p.off_sg[1 + 3 * p.L]);
+      m.tokens = tokens;
+      m.seeds = seeds;
+      m.seq_out = seq;
+      m.eps = eps;
       m.L = p.L; m.V = p.V; m.E = p.E; m.H = p.H; m.B = p.B; m.T = p.T;
-      const int S = p.B < kF32MaxSeq ? p.B : kF32MaxSeq;
-      const size_t lds = sizeof(float) * f32_lds_floats(p.L, p.V, p.E, p.H, p.B);
-      double flops = 0.0;
-      for (int l = 0; l < p.L; ++l)
-        flops += 2.0 * 4 * p.H * (((l == 0) ? p.E : p.H) + p.H);
-      flops = (flops + 2.0 * p.V * p.H) * double(ncols) * p.T;
+      m.pair0 = pair0;
+      m.pc = pc;
+      const int G = p.f32_g, NB = p.f32_nb, NT = p.f32_threads;
+      const size_t lds = sizeof(float) * f32_lds_layout(p.L, p.V, p.E, p.H, G, NB, NT).total;
+      // Matrix-product flops actually executed: every timestep, except W_hh h at t = 0 (h = 0).
+      double per_token = 2.0 * p.V * p.H, first = 0.0;
+      for (int l = 0; l < p.L; ++l) {
+        per_token += 2.0 * 4 * p.H * (((l == 0) ? p.E : p.H) + p.H);
+        first += 2.0 * 4 * p.H * p.H;
+      }
+      const double flops = (per_token * p.T - first) * double(ncols);
+      const dim3 grid(static_cast<uint32_t>((pc + G - 1) / G), static_cast<uint32_t>((p.B + NB - 1) / NB));
       CDRGE_TRY(timed(ctx, 0, flops, [&] {
-        hipLaunchKernelGGL(k_lstm_f32, dim3(pc, (p.B + S - 1) / S), dim3(kF32Threads), lds, s, m, tokens,
-                           seeds, pair0, eps, seq);
+        hipLaunchKernelGGL(f32_kernel(G, NB), grid, dim3(NT), lds, s, m);
       }));
     } else {
       const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
@@ -444,9 +500,10 @@ cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   static_cast<int>(update_lut_bytes(kUpdLutMaxProbes))));
   } else {
-    const int lds = static_cast<int>(sizeof(float) * f32_lds_floats(cfg->n_layers, cfg->vocab, cfg->embed,
-                                                                    cfg->hidden, cfg->batch));
-    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_f32),
+    const Plan& p = ctx->plan;
+    const int lds = static_cast<int>(
+        sizeof(float) * f32_lds_layout(p.L, p.V, p.E, p.H, p.f32_g, p.f32_nb, p.f32_threads).total);
+    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(f32_kernel(p.f32_g, p.f32_nb)),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   }
   uint32_t* flags = ctx->at<uint32_t>(ctx->plan.off_flags);

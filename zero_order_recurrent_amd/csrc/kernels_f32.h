@@ -1,13 +1,23 @@
-// fp32 models (small hidden sizes, long sequences, many probes): one persistent workgroup per
-// (probe pair, group of up to 8 sequences) runs the whole perturbed forward of both the +eps and
-// the -eps model - every timestep, every layer, the logits and the cross-entropy - with the
-// recurrent state in LDS. The models are independent, so no inter-workgroup synchronisation is
-// needed and a whole probe chunk is one launch.
+// fp32 models (small hidden sizes, long sequences, many probes). One persistent workgroup per
+// (G probe pairs, NB sequences) runs the whole perturbed forward of the 2G models - every
+// timestep, every layer, the logits and the cross-entropy - with the recurrent state in LDS. The
+// models are independent, so no inter-workgroup synchronisation is needed and a probe chunk is
+// one launch.
 //
 // Model (LSTM language model; the pages' "large LSTMs" on next-character prediction, pith.science
 // review Figure 2 caption): gates = W_ih x + W_hh h + b in row order i, f, g, o; c = f c + i g;
 // h = o tanh(c); logits = W_out h + b_out; loss = logsumexp - logit of the next token.
-// Perturbed weight: float(w) + (+-eps) with the sign of probe p_i (include/cdrge.h).
+// Perturbed weight: float(w) + (+-eps) with the sign of probe p_i (include/cdrge.h), rounded once
+// in fp32, as a Rademacher perturbation of every weight (pith.science review, "What carries the
+// argument").
+//
+// Work split. A thread owns one weight row (a gate row, or a logit row and a slice of its
+// columns) and computes that row's dot products for all 2G*NB (model, sequence) slots of the
+// workgroup, so each weight is loaded once for 2G models and its two perturbed values w +- eps
+// are formed once per pair. Weights are read from per-step k-major copies W^T (lanes hold
+// consecutive rows, so every load is coalesced) and the sign bits from per-chunk tables of
+// Philox words, one word per (pair, row, 32 columns), also row-fastest. Activations live in LDS
+// as [k][slot], so a single broadcast read returns the inputs of every slot for one k.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,181 +26,324 @@
 
 namespace cdrge {
 
-constexpr int kF32Threads = 256;
-constexpr int kF32MaxSeq = 8;  // sequences per workgroup
+constexpr int kF32MaxThreads = 1024;
+constexpr int kF32MaxLayers = 8;
+constexpr int kF32MaxSeq = 8;  // NB: sequences per workgroup
 
-struct F32Model {
-  const float* theta;  // flat parameters
-  int64_t off_emb, off_wout, off_bout;
-  int64_t off_wih[8], off_whh[8], off_b[8];
+// out[c][r] = in[r][c] for a row-major fp32 matrix [rows][cols]; 32 x 32 tiles through LDS.
+// grid (ceil(cols / 32), ceil(rows / 32)), 256 threads.
+__global__ __launch_bounds__(256) void k_transpose_f32(const float* __restrict__ in, int rows, int cols,
+                                                       float* __restrict__ out) {
+  __shared__ float tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int j = ty; j < 32; j += 8) {
+    const int r = r0 + j, c = c0 + tx;
+    if (r < rows && c < cols) tile[j][tx] = in[static_cast<int64_t>(r) * cols + c];
+  }
+  __syncthreads();
+  for (int j = ty; j < 32; j += 8) {
+    const int c = c0 + j, r = r0 + tx;
+    if (r < rows && c < cols) out[static_cast<int64_t>(c) * rows + r] = tile[tx][j];
+  }
+}
+
+struct F32Args {
+  const float* theta;                       // flat parameters: embedding and biases are read here
+  int64_t off_emb, off_bout, off_b[kF32MaxLayers];
+  const float* wt_ih[kF32MaxLayers];        // W_ih^T [in_l][4H]
+  const float* wt_hh[kF32MaxLayers];        // W_hh^T [H][4H]
+  const float* wt_out;                      // W_out^T [H][V]
+  const uint32_t* sg_ih[kF32MaxLayers];     // sign words [pairs][ceil(in_l / 32)][4H]
+  const uint32_t* sg_hh[kF32MaxLayers];     // [pairs][ceil(H / 32)][4H]
+  const uint32_t* sg_out;                   // [pairs][ceil(H / 32)][V]
+  const int32_t* tokens;                    // [B][T+1]
+  const uint64_t* seeds;                    // all K seeds
+  float* seq_out;                           // [2 pc][B]: per (model, sequence) sum over t of the CE
+  float eps;
   int L, V, E, H, B, T;
+  int pair0, pc;                            // the chunk's first pair and pair count
 };
 
-// Dot products of one weight row (perturbed both ways) with the inputs of both models for nb
-// sequences: acc[s][b] += sum_k (w_k + s*e_k) * x[s][b][k], k in [0, n), ascending.
-__device__ __forceinline__ void f32_row_dot(const float* __restrict__ wrow, int n, uint64_t seed,
-                                            uint32_t tensor, uint32_t row, float eps,
-                                            const float* __restrict__ x, int x_stride_seq,
-                                            int x_stride_side, int nb, float (&acc)[2][kF32MaxSeq]) {
-  PhiloxOut o{0, 0, 0, 0};
-  for (int k = 0; k < n; ++k) {
-    if ((k & 127) == 0) o = sign_block(seed, tensor, row, static_cast<uint32_t>(k >> 7));
-    const uint32_t word = pick_word(o, static_cast<uint32_t>((k >> 5) & 3));
-    const uint32_t bit = (word >> sign_bit_pos(static_cast<uint32_t>(k))) & 1u;
-    const float w = wrow[k];
-    const float e = signed_eps(eps, bit);
-    const float wp = w + e;
-    const float wm = w - e;
+// Offsets (in floats) of the LDS regions; every region starts on a 16-byte boundary.
+struct F32Lds {
+  int h, c, xin, gbuf, bias, bout, z, loss, total;
+};
+__host__ __device__ inline int f32_pad4(int x) { return (x + 3) & ~3; }
+__host__ __device__ inline F32Lds f32_lds_layout(int L, int V, int E, int H, int G, int NB, int NT) {
+  const int M = 2 * G * NB, G4 = 4 * H;
+  F32Lds o;
+  int at = 0;
+  o.h = at;    at += f32_pad4(L * H * M);                 // [L][H][M]
+  o.c = at;    at += f32_pad4(L * H * M);                 // [L][H][M]
+  o.xin = at;  at += f32_pad4(E * M);                     // [E][M]
+  const int grows = G4 > NT ? (G4 > V ? G4 : V) : (NT > V ? NT : V);
+  o.gbuf = at; at += f32_pad4(grows * M);                 // gates [4H][M], then logit partials [slice][V][M]
+  o.bias = at; at += f32_pad4(L * G4 * 2 * G);            // [L][4H][2G]
+  o.bout = at; at += f32_pad4(V * 2 * G);                 // [V][2G]
+  o.z = at;    at += f32_pad4(V * M);                     // [V][M]
+  o.loss = at; at += f32_pad4(M);                         // [M]
+  o.total = at;
+  return o;
+}
+
+// Threads of a workgroup: one per gate row, rounded up to whole waves, at most 1024.
+inline int f32_threads(int H) {
+  const int r = ((4 * H + 63) / 64) * 64;
+  return r < kF32MaxThreads ? r : kF32MaxThreads;
+}
+
+template <int M>
+__device__ __forceinline__ void f32_load_slots(const float* p, float (&v)[M]) {
+  if constexpr (M % 4 == 0) {
 #pragma unroll
-    for (int b = 0; b < kF32MaxSeq; ++b) {
-      if (b < nb) {
-        acc[0][b] = fmaf(wp, x[b * x_stride_seq + k], acc[0][b]);
-        acc[1][b] = fmaf(wm, x[x_stride_side + b * x_stride_seq + k], acc[1][b]);
+    for (int i = 0; i < M / 4; ++i) {
+      const float4 t = reinterpret_cast<const float4*>(p)[i];
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+  } else {
+    static_assert(M == 2, "slot counts are 2, 4, 8 or 16");
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  }
+}
+template <int M>
+__device__ __forceinline__ void f32_store_slots(float* p, const float (&v)[M]) {
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < M / 4; ++i)
+      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  }
+}
+
+// One column k of the perturbed dot products of row r: for pair g with sign bit s (bit p of
+// word[g]; set = -1), the +eps model takes w + s eps and the -eps model w - s eps.
+template <int G, int NB>
+__device__ __forceinline__ void f32_column(float (&acc)[2 * G * NB], float w, const float* xk,
+                                           const uint32_t (&word)[G], uint32_t p, float eps) {
+  constexpr int M = 2 * G * NB;
+  float xv[M];
+  f32_load_slots<M>(xk, xv);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float e = __uint_as_float(__float_as_uint(eps) ^ ((word[g] << (31u - p)) & 0x80000000u));
+    const float wp = w + e, wm = w - e;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc[(2 * g) * NB + b] = fmaf(wp, xv[(2 * g) * NB + b], acc[(2 * g) * NB + b]);
+      acc[(2 * g + 1) * NB + b] = fmaf(wm, xv[(2 * g + 1) * NB + b], acc[(2 * g + 1) * NB + b]);
+    }
+  }
+}
+
+// acc[slot] += sum_k (W[r][k] +- eps p(r, k)) x[k][slot] for k in [0, K): wt is W^T with `ld`
+// rows per column (wt[k * ld + r] = W[r][k]), sg the tensor's sign table with `ld` rows, x the
+// activations in LDS as [K][M]. Columns go in ascending order.
+template <int G, int NB>
+__device__ __forceinline__ void f32_row_dot(float (&acc)[2 * G * NB], const float* __restrict__ wt,
+                                            const uint32_t* __restrict__ sg, int ld, int r, int K,
+                                            const float* x, const int (&qg)[G], float eps) {
+  constexpr int M = 2 * G * NB;
+  const int nw = (K + 31) >> 5;
+  for (int kw = 0; kw < nw; ++kw) {
+    uint32_t word[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) word[g] = (sg + (static_cast<int64_t>(qg[g]) * nw + kw) * ld)[r];
+    const int k0 = 32 * kw;
+    if (k0 + 32 <= K) {
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) {
+        const int k = k0 + kk;
+        const float w = (wt + static_cast<int64_t>(k) * ld)[r];
+        f32_column<G, NB>(acc, w, x + k * M, word, static_cast<uint32_t>((kk >> 1) | ((kk & 1) << 4)), eps);
+      }
+    } else {
+      for (int k = k0; k < K; ++k) {
+        const float w = (wt + static_cast<int64_t>(k) * ld)[r];
+        f32_column<G, NB>(acc, w, x + k * M, word, sign_bit_pos(static_cast<uint32_t>(k)), eps);
       }
     }
   }
 }
 
-// grid: (pairs in chunk, ceil(B / S)), S = min(B, kF32MaxSeq). Dynamic LDS: see layout below.
-// seq_out[(2 q + s) * B + b] = sum_t cross-entropy of model (pair q, side s) on sequence b.
-__global__ __launch_bounds__(kF32Threads) void k_lstm_f32(F32Model m, const int32_t* __restrict__ tokens,
-                                                        const uint64_t* __restrict__ seeds, int pair0,
-                                                        float eps, float* __restrict__ seq_out) {
-  extern __shared__ float lds[];
-  const int tid = threadIdx.x;
-  const int q = blockIdx.x;
-  const int S = min(kF32MaxSeq, m.B);  // sequences per workgroup (LDS is laid out for S)
-  const int b0 = blockIdx.y * S;
-  const int nb = min(S, m.B - b0);
-  const uint64_t seed = seeds[pair0 + q];
-  const int L = m.L, V = m.V, E = m.E, H = m.H, G = 4 * H;
-  const int X = max(E, H);
+// grid (ceil(pc / G), ceil(B / NB)); block f32_threads(H); dynamic LDS f32_lds_layout(...).total
+// floats. Slot (g, s, b) = (2g + s) NB + b is sequence b0 + b of model (pair q0 + g, side s).
+// A workgroup whose last pair slot has no pair (pc odd) repeats its previous pair there and does
+// not write it; slots past the batch compute on zero inputs and are not written either.
+template <int G, int NB>
+__global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
+  constexpr int M = 2 * G * NB;
+  extern __shared__ __align__(16) float lds[];
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int L = a.L, V = a.V, E = a.E, H = a.H, G4 = 4 * H;
+  const F32Lds lay = f32_lds_layout(L, V, E, H, G, NB, NT);
+  float* h = lds + lay.h;
+  float* c = lds + lay.c;
+  float* xin = lds + lay.xin;
+  float* gbuf = lds + lay.gbuf;
+  float* bias = lds + lay.bias;
+  float* bout = lds + lay.bout;
+  float* z = lds + lay.z;
+  float* loss = lds + lay.loss;
 
-  // LDS layout (floats). Per-side blocks are [S][len].
-  float* h = lds;                                  // [L][2][S][H]
-  float* c = h + L * 2 * S * H;           // [L][2][S][H]
-  float* gates = c + L * 2 * S * H;       // [2][S][G]
-  float* xin = gates + 2 * S * G;         // [2][S][X]
-  float* bias = xin + 2 * S * X;          // [L][2][G]
-  float* bout = bias + L * 2 * G;                  // [2][V]
-  float* z = bout + 2 * V;                         // [2][S][V]
-  float* loss = z + 2 * S * V;            // [2][S]
+  const int q0 = blockIdx.x * G;
+  const int b0 = blockIdx.y * NB;
+  const int nb = min(NB, a.B - b0);
+  int qg[G];
+  uint64_t seed[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qg[g] = min(q0 + g, a.pc - 1);
+    seed[g] = a.seeds[a.pair0 + qg[g]];
+  }
 
-  for (int i = tid; i < L * 2 * S * H; i += kF32Threads) {
+  for (int i = tid; i < L * H * M; i += NT) {
     h[i] = 0.f;
     c[i] = 0.f;
   }
-  if (tid < 2 * S) loss[tid] = 0.f;
-  // Perturbed biases of both models, once.
-  for (int l = 0; l < L; ++l) {
-    for (int r = tid; r < G; r += kF32Threads) {
-      const PhiloxOut o = sign_block(seed, 3u + 3u * l, 0u, static_cast<uint32_t>(r >> 7));
-      const uint32_t bit = (pick_word(o, (r >> 5) & 3) >> sign_bit_pos(r)) & 1u;
-      const float e = signed_eps(eps, bit);
-      const float w = m.theta[m.off_b[l] + r];
-      bias[(l * 2 + 0) * G + r] = w + e;
-      bias[(l * 2 + 1) * G + r] = w - e;
-    }
+  if (tid < M) loss[tid] = 0.f;
+  // Perturbed biases of both models of every pair, once.
+  for (int i = tid; i < L * G4 * G; i += NT) {
+    const int g = i % G, r = (i / G) % G4, l = i / (G * G4);
+    const PhiloxOut o = sign_block(seed[g], 3u + 3u * l, 0u, static_cast<uint32_t>(r >> 7));
+    const uint32_t bit = (pick_word(o, (r >> 5) & 3) >> sign_bit_pos(r)) & 1u;
+    const float e = signed_eps(a.eps, bit);
+    const float w = a.theta[a.off_b[l] + r];
+    bias[(l * G4 + r) * 2 * G + 2 * g] = w + e;
+    bias[(l * G4 + r) * 2 * G + 2 * g + 1] = w - e;
   }
-  for (int v = tid; v < V; v += kF32Threads) {
-    const PhiloxOut o = sign_block(seed, 2u + 3u * L, 0u, static_cast<uint32_t>(v >> 7));
+  for (int i = tid; i < V * G; i += NT) {
+    const int g = i % G, v = i / G;
+    const PhiloxOut o = sign_block(seed[g], 2u + 3u * L, 0u, static_cast<uint32_t>(v >> 7));
     const uint32_t bit = (pick_word(o, (v >> 5) & 3) >> sign_bit_pos(v)) & 1u;
-    const float e = signed_eps(eps, bit);
-    const float w = m.theta[m.off_bout + v];
-    bout[v] = w + e;
-    bout[V + v] = w - e;
+    const float e = signed_eps(a.eps, bit);
+    const float w = a.theta[a.off_bout + v];
+    bout[v * 2 * G + 2 * g] = w + e;
+    bout[v * 2 * G + 2 * g + 1] = w - e;
   }
-  __syncthreads();
 
-  for (int t = 0; t < m.T; ++t) {
-    // Layer-0 input: perturbed embedding rows of the current tokens.
-    for (int i = tid; i < nb * E; i += kF32Threads) {
-      const int b = i / E, e = i % E;
-      int tok = tokens[static_cast<int64_t>(b0 + b) * (m.T + 1) + t];
-      tok = min(max(tok, 0), V - 1);  // invalid tokens are reported through the loss (NaN)
-      const PhiloxOut o = sign_block(seed, 0u, static_cast<uint32_t>(tok), static_cast<uint32_t>(e >> 7));
-      const uint32_t bit = (pick_word(o, (e >> 5) & 3) >> sign_bit_pos(e)) & 1u;
-      const float ee = signed_eps(eps, bit);
-      const float w = m.theta[m.off_emb + static_cast<int64_t>(tok) * E + e];
-      xin[(0 * S + b) * X + e] = w + ee;
-      xin[(1 * S + b) * X + e] = w - ee;
+  const int nsl = max(1, NT / V);            // column slices of the logits
+  const int kper = (H + nsl - 1) / nsl;
+  for (int t = 0; t < a.T; ++t) {
+    // Layer-0 input: the perturbed embedding rows of the current tokens.
+    for (int i = tid; i < E * M; i += NT) {
+      const int slot = i % M, e = i / M;
+      const int g = slot / (2 * NB), s = (slot / NB) & 1, b = slot % NB;
+      float v = 0.f;
+      if (b < nb) {
+        int tok = a.tokens[static_cast<int64_t>(b0 + b) * (a.T + 1) + t];
+        tok = min(max(tok, 0), V - 1);  // invalid tokens are reported through the loss (NaN)
+        const PhiloxOut o = sign_block(seed[g], 0u, static_cast<uint32_t>(tok), static_cast<uint32_t>(e >> 7));
+        const uint32_t bit = (pick_word(o, (e >> 5) & 3) >> sign_bit_pos(e)) & 1u;
+        const float ee = signed_eps(a.eps, bit);
+        const float w = a.theta[a.off_emb + static_cast<int64_t>(tok) * E + e];
+        v = s ? w - ee : w + ee;
+      }
+      xin[e * M + slot] = v;
     }
     __syncthreads();
     for (int l = 0; l < L; ++l) {
       const int in = (l == 0) ? E : H;
-      const float* x = (l == 0) ? xin : (h + (l - 1) * 2 * S * H);
-      const int xs = (l == 0) ? X : H;
-      const float* hl = h + l * 2 * S * H;
-      for (int r = tid; r < G; r += kF32Threads) {
-        float acc[2][kF32MaxSeq];
+      const float* x = (l == 0) ? xin : h + (l - 1) * H * M;
+      const float* hl = h + l * H * M;
+      for (int r = tid; r < G4; r += NT) {
+        float acc[M];
 #pragma unroll
-        for (int b = 0; b < kF32MaxSeq; ++b) acc[0][b] = acc[1][b] = 0.f;
-        f32_row_dot(m.theta + m.off_wih[l] + static_cast<int64_t>(r) * in, in, seed, 1u + 3u * l,
-                    static_cast<uint32_t>(r), eps, x, xs, S * xs, nb, acc);
-        f32_row_dot(m.theta + m.off_whh[l] + static_cast<int64_t>(r) * H, H, seed, 2u + 3u * l,
-                    static_cast<uint32_t>(r), eps, hl, H, S * H, nb, acc);
-        for (int b = 0; b < nb; ++b) {
-          gates[(0 * S + b) * G + r] = acc[0][b] + bias[(l * 2 + 0) * G + r];
-          gates[(1 * S + b) * G + r] = acc[1][b] + bias[(l * 2 + 1) * G + r];
+        for (int i = 0; i < M; ++i) acc[i] = 0.f;
+        f32_row_dot<G, NB>(acc, a.wt_ih[l], a.sg_ih[l], G4, r, in, x, qg, a.eps);
+        if (t > 0) f32_row_dot<G, NB>(acc, a.wt_hh[l], a.sg_hh[l], G4, r, H, hl, qg, a.eps);
+        const float* bs = bias + (l * G4 + r) * 2 * G;
+#pragma unroll
+        for (int i = 0; i < M; ++i) acc[i] += bs[i / NB];
+        f32_store_slots<M>(gbuf + r * M, acc);
+      }
+      __syncthreads();
+      float* cl = c + l * H * M;
+      float* hw = h + l * H * M;
+      for (int i = tid; i < H * M; i += NT) {
+        const float gi = gbuf[i], gf = gbuf[H * M + i], gg = gbuf[2 * H * M + i], go = gbuf[3 * H * M + i];
+        const float ig = 1.f / (1.f + expf(-gi));
+        const float fg = 1.f / (1.f + expf(-gf));
+        const float gt = tanhf(gg);
+        const float og = 1.f / (1.f + expf(-go));
+        const float cn = fg * cl[i] + ig * gt;
+        cl[i] = cn;
+        hw[i] = og * tanhf(cn);
+      }
+      __syncthreads();
+    }
+    // Logits: thread (row v, column slice j) forms a partial dot product over its slice.
+    const float* hl = h + (L - 1) * H * M;
+    for (int i = tid; i < nsl * V; i += NT) {
+      const int v = i % V, j = i / V;
+      const int k0 = j * kper, k1 = min(H, k0 + kper);
+      const int nw = (H + 31) >> 5;
+      float acc[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) acc[i] = 0.f;
+      uint32_t word[G];
+      for (int k = k0; k < k1; ++k) {
+        if (k == k0 || (k & 31) == 0) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) word[g] = (a.sg_out + (static_cast<int64_t>(qg[g]) * nw + (k >> 5)) * V)[v];
         }
+        const float w = (a.wt_out + static_cast<int64_t>(k) * V)[v];
+        f32_column<G, NB>(acc, w, hl + k * M, word, sign_bit_pos(static_cast<uint32_t>(k)), a.eps);
       }
-      __syncthreads();
-      float* cl = c + l * 2 * S * H;
-      float* hw = h + l * 2 * S * H;
-      for (int i = tid; i < 2 * nb * H; i += kF32Threads) {
-        const int s = i / (nb * H), b = (i / H) % nb, j = i % H;
-        const float* g = gates + (s * S + b) * G;
-        const float ig = 1.f / (1.f + expf(-g[j]));
-        const float fg = 1.f / (1.f + expf(-g[H + j]));
-        const float gg = tanhf(g[2 * H + j]);
-        const float og = 1.f / (1.f + expf(-g[3 * H + j]));
-        const int sidx = (s * S + b) * H + j;
-        const float cn = fg * cl[sidx] + ig * gg;
-        cl[sidx] = cn;
-        hw[sidx] = og * tanhf(cn);
-      }
-      __syncthreads();
-    }
-    // Logits of both models from the last layer.
-    const float* hl = h + (L - 1) * 2 * S * H;
-    for (int v = tid; v < V; v += kF32Threads) {
-      float acc[2][kF32MaxSeq];
-#pragma unroll
-      for (int b = 0; b < kF32MaxSeq; ++b) acc[0][b] = acc[1][b] = 0.f;
-      f32_row_dot(m.theta + m.off_wout + static_cast<int64_t>(v) * H, H, seed, 1u + 3u * L,
-                  static_cast<uint32_t>(v), eps, hl, H, S * H, nb, acc);
-      for (int b = 0; b < nb; ++b) {
-        z[(0 * S + b) * V + v] = acc[0][b] + bout[v];
-        z[(1 * S + b) * V + v] = acc[1][b] + bout[V + v];
-      }
+      f32_store_slots<M>(gbuf + (j * V + v) * M, acc);
     }
     __syncthreads();
-    if (tid < 2 * nb) {
-      const int s = tid / nb, b = tid % nb;
-      const float* zz = z + (s * S + b) * V;
-      float zmax = zz[0];
-      for (int v = 1; v < V; ++v) zmax = fmaxf(zmax, zz[v]);
-      float sum = 0.f;
-      for (int v = 0; v < V; ++v) sum += expf(zz[v] - zmax);
-      int y = tokens[static_cast<int64_t>(b0 + b) * (m.T + 1) + t + 1];
-      y = min(max(y, 0), V - 1);
-      loss[s * S + b] += (zmax + logf(sum)) - zz[y];
+    for (int i = tid; i < V * M; i += NT) {
+      const int v = i / M, slot = i % M;
+      float s = bout[v * 2 * G + slot / NB];
+      for (int j = 0; j < nsl; ++j) s += gbuf[(j * V + v) * M + slot];
+      z[i] = s;
     }
     __syncthreads();
+    // Cross-entropy per slot. The next writes of z and gbuf come after the next barriers.
+    if (tid < M) {
+      const int slot = tid, b = slot % NB;
+      if (b < nb) {
+        float zmax = z[slot];
+        for (int v = 1; v < V; ++v) zmax = fmaxf(zmax, z[v * M + slot]);
+        float sum = 0.f;
+        for (int v = 0; v < V; ++v) sum += expf(z[v * M + slot] - zmax);
+        int y = a.tokens[static_cast<int64_t>(b0 + b) * (a.T + 1) + t + 1];
+        y = min(max(y, 0), V - 1);
+        loss[slot] += (zmax + logf(sum)) - z[y * M + slot];
+      }
+    }
   }
-  if (tid < 2 * nb) {
-    const int s = tid / nb, b = tid % nb;
-    seq_out[static_cast<int64_t>(2 * q + s) * m.B + b0 + b] = loss[s * S + b];
+  __syncthreads();
+  if (tid < M) {
+    const int slot = tid, g = slot / (2 * NB), s = (slot / NB) & 1, b = slot % NB;
+    if (b < nb && q0 + g < a.pc)
+      a.seq_out[static_cast<int64_t>(2 * (q0 + g) + s) * a.B + b0 + b] = loss[slot];
   }
 }
 
-// Floats of dynamic LDS k_lstm_f32 needs.
+// Sequences per workgroup for a batch of B, and pairs per workgroup for a chunk of P pairs: two
+// pairs share each weight load when the chunk has enough pairs to fill the chip twice over.
+inline int f32_nb(int B) { return B >= 8 ? 8 : (B >= 4 ? 4 : (B >= 2 ? 2 : 1)); }
+inline int f32_g(int NB, int P) { return (NB <= 4 && P >= 512) ? 2 : 1; }
 
-inline int64_t f32_lds_floats(int L, int V, int E, int H, int B) {
-  const int64_t S = B < kF32MaxSeq ? B : kF32MaxSeq;
-  const int64_t G = 4 * int64_t(H), X = (E > H ? E : H);
-  return 2 * int64_t(L) * 2 * S * H + 2 * S * G + 2 * S * X + int64_t(L) * 2 * G + 2 * V +
-         2 * S * V + 2 * S;
+typedef void (*F32Kernel)(F32Args);
+inline F32Kernel f32_kernel(int G, int NB) {
+  if (G == 2) {
+    switch (NB) {
+      case 1: return k_lstm_f32<2, 1>;
+      case 2: return k_lstm_f32<2, 2>;
+      default: return k_lstm_f32<2, 4>;
+    }
+  }
+  switch (NB) {
+    case 1: return k_lstm_f32<1, 1>;
+    case 2: return k_lstm_f32<1, 2>;
+    case 4: return k_lstm_f32<1, 4>;
+    default: return k_lstm_f32<1, 8>;
+  }
 }
 
 }  // namespace cdrge
