@@ -382,10 +382,10 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       const dim3 cgrid((p.B + kCeCols - 1) / kCeCols, pc);
       for (int t = 0; t < p.T; ++t) {
         {
-          const int64_t n = int64_t(ncols + kTileCols) * (p.E / 8);
+          const int64_t n = p.ncols_pad * (p.E / 8);
           CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
             hipLaunchKernelGGL(k_gather_x0, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, emb_m,
-                               tokens, p.B, p.T, t, p.V, p.E, ncols, ncols + kTileCols, x0);
+                               tokens, p.B, p.T, t, p.V, p.E, ncols, static_cast<int>(p.ncols_pad), x0);
           }));
         }
         for (int l = 0; l < p.L; ++l) {
@@ -404,6 +404,7 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           g.bias_m = bias_m;
           g.in = static_cast<int>(tih.cols);
           g.H = p.H; g.B = p.B; g.L = p.L;
+          g.ncols_pad = static_cast<int>(p.ncols_pad);
           g.layer = l;
           g.first = (t == 0) ? 1 : 0;
           g.n_row_tiles = n_rt;
@@ -426,6 +427,7 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
         ce.seq = seq;
         ce.pair0 = pair0;
         ce.H = p.H; ce.B = p.B; ce.V = p.V; ce.T = p.T; ce.t = t;
+        ce.ncols_pad = static_cast<int>(p.ncols_pad);
         ce.tensor_wout = tw.id;
         const double flops = 2.0 * p.V * p.H * double(ncols);
         CDRGE_TRY(timed(ctx, 1, flops, [&] {

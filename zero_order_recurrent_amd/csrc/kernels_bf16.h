@@ -37,12 +37,12 @@ constexpr size_t kCeLdsBytes =
 struct CeArgs {
   const uint16_t* wp;
   const uint16_t* wm;      // W_out candidates [V][H]
-  const uint16_t* h;       // last layer h_t [Ncols][H]
+  const uint16_t* h;       // last layer h_t, [H / 32][ncols_pad][32] (k-chunk-major)
   const float* bout_m;     // per-model perturbed output bias [2P][64]
   const int32_t* tokens;   // [B][T+1]
   const uint64_t* seeds;
   float* seq;              // [2P][B]
-  int pair0, H, B, V, T, t;
+  int pair0, H, B, V, T, t, ncols_pad;
   uint32_t tensor_wout;
 };
 
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint16_t* src = a.h + bcol_g[j] * H + kKChunk * c + 8 * bq;
+      const uint16_t* src = a.h + (static_cast<int64_t>(c) * a.ncols_pad + bcol_g[j]) * kKChunk + 8 * bq;
       rb[j] = bvalid[j] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
     }
   };

@@ -132,25 +132,27 @@ __global__ void k_model_tensor_bf16(const uint16_t* __restrict__ src, int rows, 
   }
 }
 
-// Layer-0 input of timestep t for every (model, sequence) column of a chunk:
-// x[m * B + b][:] = emb_m[m][token(b, t)][:], the model's perturbed embedding row, so that the
-// gate kernel reads its input operand as [columns][E] exactly like the h of a lower layer.
+// Layer-0 input of timestep t for every (model, sequence) column of a chunk: column m * B + b
+// holds emb_m[m][token(b, t)][:], the model's perturbed embedding row, stored k-chunk-major
+// like the h of a lower layer (element (column, e) at ((e / 32) ncols_pad + column) 32 + e % 32).
 // Columns ncols .. ncols_pad - 1 are zero. Tokens outside [0, V) are clamped (the step's losses
-// are NaN then anyway). One thread per 16-byte piece (E % 8 == 0).
+// are NaN then anyway). One thread per 16-byte piece (E % 32 == 0); consecutive threads write
+// consecutive pieces.
 __global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* __restrict__ tokens, int B,
                             int T, int t, int V, int E, int ncols, int ncols_pad, uint16_t* __restrict__ x) {
-  const int pieces = E / 8;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= static_cast<int64_t>(ncols_pad) * pieces) return;
-  const int col = static_cast<int>(i / pieces), pc = static_cast<int>(i % pieces);
+  if (i >= static_cast<int64_t>(E / 8) * ncols_pad) return;
+  const int p4 = static_cast<int>(i & 3);
+  const int64_t rc = i >> 2;  // (e / 32) * ncols_pad + column
+  const int col = static_cast<int>(rc % ncols_pad), kc = static_cast<int>(rc / ncols_pad);
   uint4 v = make_uint4(0, 0, 0, 0);
   if (col < ncols) {
     const int m = col / B, b = col % B;
     int tok = tokens[static_cast<int64_t>(b) * (T + 1) + t];
     tok = min(max(tok, 0), V - 1);
-    v = reinterpret_cast<const uint4*>(emb_m + (static_cast<int64_t>(m) * V + tok) * E)[pc];
+    v = reinterpret_cast<const uint4*>(emb_m + (static_cast<int64_t>(m) * V + tok) * E)[4 * kc + p4];
   }
-  reinterpret_cast<uint4*>(x + static_cast<int64_t>(col) * E)[pc] = v;
+  reinterpret_cast<uint4*>(x)[i] = v;
 }
 
 // losses[m0 + m] = (sum_b seq[m][b]) / (B T) with a fixed-order double reduction (bitwise

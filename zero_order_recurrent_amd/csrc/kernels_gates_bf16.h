@@ -104,13 +104,13 @@ struct GateArgs {
   const uint16_t* w_hh;    // W_hh [4H][H]
   const uint32_t* sg_ih;   // sign words of W_ih for the chunk's pairs, [pairs][in / 32][4H]
   const uint32_t* sg_hh;   // sign words of W_hh, [pairs][H / 32][4H]
-  const uint16_t* x_in;    // input of this layer at t, [columns][in] (padded columns readable)
-  const uint16_t* h_prev;  // this layer's h_{t-1}, [columns][H] (unused when first)
-  uint16_t* h_out;         // this layer's h_t, [columns][H]
+  const uint16_t* x_in;    // input of this layer at t, [in / 32][ncols_pad][32] (k-chunk-major)
+  const uint16_t* h_prev;  // this layer's h_{t-1}, [H / 32][ncols_pad][32] (unused when first)
+  uint16_t* h_out;         // this layer's h_t, [H / 32][ncols_pad][32]
   float* c_tile;           // this layer's cell state in accumulator order, 64 KB per tile
   const float* bias_m;     // per-model perturbed gate bias [2P][L][4H]
   float eps;
-  int in, H, B, L, layer, first;
+  int in, H, B, L, layer, first, ncols_pad;
   int n_row_tiles, n_col_blocks, n_pairs, swizzle;
 };
 
@@ -163,13 +163,15 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   const uint32_t* sgh = a.sg_hh + static_cast<int64_t>(pr) * (H / kKChunk) * (4 * H) + grow;
 
   // ---- activation operand of this wave: lane holds column 64 cq + 16 j + lane % 16 of model
-  // m_out, k piece lane / 16 (the MFMA B layout). Columns past the batch read the padding or the
-  // next model's columns (results unused). Element offsets are 32-bit: the host guarantees that
-  // the padded column count times max(in, H) fits.
+  // m_out, k piece lane / 16 (the MFMA B layout). Activations are stored k-chunk-major, element
+  // (column, k) at ((k / 32) ncols_pad + column) 32 + k % 32, so the 16 columns of one fragment
+  // are 1 KB of contiguous memory. Columns past the batch read the padding or the next model's
+  // columns (results unused). Element offsets are 32-bit: the host guarantees that the padded
+  // column count times max(in, H) fits.
   const int kp = lane >> 4;
   const uint32_t gcol0 = static_cast<uint32_t>(m_out * a.B + bcol0 + 64 * cq + (lane & 15));
-  const uint32_t xoff = gcol0 * static_cast<uint32_t>(a.in) + 8 * kp;
-  const uint32_t hoff = gcol0 * static_cast<uint32_t>(H) + 8 * kp;
+  const uint32_t boff = gcol0 * kKChunk + 8 * kp;
+  const int64_t chunk_stride = static_cast<int64_t>(a.ncols_pad) * kKChunk;
 
   const int kx = a.in / kKChunk;
   const int kh = a.first ? 0 : H / kKChunk;
@@ -227,19 +229,17 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[j], acc[i][j], 0, 0, 0);
   };
-  // Activations of chunks c and c+1 (c even), fragment by fragment, so that the two 64-byte
-  // halves of every 128-byte line go out in consecutive loads and the L1 fetches the line once.
+  // Activations of chunks c and c+1 (c even): fragment j of a chunk is the 16 columns
+  // 16 j .. 16 j + 15 of the wave, 512 elements further per fragment.
   auto load_b_pair = [&](int c, bf16x8 (&d0)[4], bf16x8 (&d1)[4]) {
     const int c0 = min(c, nch - 1), c1 = min(c + 1, nch - 1);
     const bool x0p = c0 < kx, x1p = c1 < kx;
-    const uint16_t* s0 = (x0p ? a.x_in : a.h_prev) + kKChunk * (x0p ? c0 : c0 - kx);
-    const uint16_t* s1 = (x1p ? a.x_in : a.h_prev) + kKChunk * (x1p ? c1 : c1 - kx);
-    const int ld0 = x0p ? a.in : H, ld1 = x1p ? a.in : H;
-    const uint32_t o0 = x0p ? xoff : hoff, o1 = x1p ? xoff : hoff;
+    const uint16_t* s0 = (x0p ? a.x_in : a.h_prev) + chunk_stride * (x0p ? c0 : c0 - kx);
+    const uint16_t* s1 = (x1p ? a.x_in : a.h_prev) + chunk_stride * (x1p ? c1 : c1 - kx);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      d0[j] = *reinterpret_cast<const bf16x8*>(s0 + 16 * j * ld0 + o0);
-      d1[j] = *reinterpret_cast<const bf16x8*>(s1 + 16 * j * ld1 + o1);
+      d0[j] = *reinterpret_cast<const bf16x8*>(s0 + 16 * kKChunk * j + boff);
+      d1[j] = *reinterpret_cast<const bf16x8*>(s1 + 16 * kKChunk * j + boff);
     }
   };
 
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     if (b < a.B) {
       const int64_t gcol = static_cast<int64_t>(2 * pr + sd) * a.B + b;
       const uint4* src = reinterpret_cast<const uint4*>(Hs + cidx * kHsStride);
-      uint4* dst = reinterpret_cast<uint4*>(a.h_out + gcol * H + u0);
+      uint4* dst = reinterpret_cast<uint4*>(a.h_out + (static_cast<int64_t>(rt) * a.ncols_pad + gcol) * kKChunk);
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[v] = src[v];
     }
