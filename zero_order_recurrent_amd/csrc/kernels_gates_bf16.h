@@ -66,31 +66,19 @@ constexpr size_t kGateLdsBytes = kGateBiasOffset + sizeof(float) * 2 * 4 * kUnit
 static_assert(sizeof(uint16_t) * 2 * kTileCols * kHsStride <= kGateBiasOffset,
               "the h transpose buffer reuses the weight ring");
 
-__device__ __forceinline__ float fast_sigmoid(float x) {
-  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+// LSTM cell from the four gate pre-activations: sigmoid(x) = 1 / (1 + e^-x),
+// tanh(x) = 2 / (1 + e^-2x) - 1, c' = sigmoid(f) c + sigmoid(i) tanh(g), h = sigmoid(o) tanh(c').
+// Written this way the functions saturate correctly without clamping (e^-x = inf gives 0 and
+// -1) and a NaN argument stays NaN; each cell costs 5 exponentials and 5 reciprocals.
+__device__ __forceinline__ float cell_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float cell_tanh(float x) {
+  return 2.f * __builtin_amdgcn_rcpf(1.f + __expf(-2.f * x)) - 1.f;
 }
-__device__ __forceinline__ float fast_tanh(float x) { return 2.f * fast_sigmoid(2.f * x) - 1.f; }
-
-// LSTM cell from the four gate pre-activations, with the reciprocals merged:
-//   sigmoid(x) = 1/(1+e^-x), tanh(x) = (1-e^-2x)/(1+e^-2x),
-//   c' = c sigmoid(f) + sigmoid(i) tanh(g) = (c A Gm + Gp F) / (F A Gm),
-//   h  = sigmoid(o) tanh(c') = (1 - e^-2c') / (O (1 + e^-2c')),
-// with A = 1+e^-i, F = 1+e^-f, Gp/Gm = 1 -/+ e^-2g, O = 1+e^-o. Arguments are clamped to
-// [-15, 15] (sigmoid(-15) = 3e-7, tanh(15) = 1 in float), which bounds every product below 1e27;
-// the clamp is written with comparisons so that a NaN argument stays NaN.
-__device__ __forceinline__ float clamp15(float x) { return x < -15.f ? -15.f : (x > 15.f ? 15.f : x); }
 __device__ __forceinline__ void lstm_cell(float gi, float gf, float gg, float go, float c, float& c_out,
                                           float& h_out) {
-  const float A = 1.f + __expf(-clamp15(gi));
-  const float F = 1.f + __expf(-clamp15(gf));
-  const float eg = __expf(-2.f * clamp15(gg));
-  const float O = 1.f + __expf(-clamp15(go));
-  const float Gm = 1.f + eg, Gp = 1.f - eg;
-  const float AG = A * Gm;
-  const float cn = (c * AG + Gp * F) * __builtin_amdgcn_rcpf(F * AG);
-  const float ec = __expf(-2.f * clamp15(cn));
+  const float cn = cell_sigmoid(gf) * c + cell_sigmoid(gi) * cell_tanh(gg);
   c_out = cn;
-  h_out = (1.f - ec) * __builtin_amdgcn_rcpf(O * (1.f + ec));
+  h_out = cell_sigmoid(go) * cell_tanh(cn);
 }
 
 // Byte offset of 16-byte piece p (k = 8p..8p+7) of row r in a tile of 64-byte rows. Pieces are
