@@ -26,6 +26,8 @@ SMALL = {
     "bf16_ragged": b.make_config(2, 50, 64, 128, 160, 3, 3, "bf16", 1e-4, 1e-4, 79, probes_per_chunk=2),
     "bf16_e32_v5": b.make_config(1, 5, 32, 64, 40, 4, 2, "bf16", 1e-2, 1e-2, 80),
     "bf16_v64": b.make_config(3, 64, 96, 192, 130, 2, 2, "bf16", 1e-3, 1e-3, 81),
+    # H = 416 (13 chunks of 32): the logits' reduction over H is split in two slices (8 + 5 chunks)
+    "bf16_ce_split": b.make_config(1, 50, 32, 416, 40, 3, 2, "bf16", 1e-4, 1e-4, 84),
 }
 
 

@@ -3,6 +3,7 @@
 // never allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -59,6 +60,8 @@ struct Plan {
   std::vector<size_t> off_sg;          // per tensor id (W_ih, W_hh; fp32 also W_out): sign words of a chunk
   std::vector<size_t> off_wt;          // per tensor id (fp32 W_ih, W_hh, W_out): k-major copy W^T
   int f32_g, f32_nb, f32_threads;      // fp32: pairs and sequences per workgroup, threads
+  int ce_slices, ce_kper;              // bf16 logits: K slices (1 = fused) and 32-wide chunks per slice
+  size_t off_zpart;                    // bf16 logits: partial logits when split
 };
 
 bool basic_valid(const cdrge_config* c) {
@@ -148,6 +151,9 @@ Plan make_plan(const cdrge_config* c) {
   p.off_wm.assign(p.tensors.size(), 0);
   p.off_sg.assign(p.tensors.size(), 0);
   p.off_wt.assign(p.tensors.size(), 0);
+  p.ce_slices = 1;
+  p.ce_kper = 0;
+  p.off_zpart = 0;
   p.f32_nb = f32_nb(p.B);
   p.f32_g = f32_g(p.f32_nb, p.P);
   p.f32_threads = f32_threads(p.H);
@@ -169,6 +175,14 @@ Plan make_plan(const cdrge_config* c) {
     p.off_x0 = region(sizeof(uint16_t) * p.ncols_pad * p.E);
     p.off_h = region(sizeof(uint16_t) * int64_t(p.L) * 2 * p.ncols_pad * p.H);
     p.off_c = region(sizeof(float) * int64_t(p.L) * p.n_tiles * kGateThreads * 32);
+    // Logits: split the reduction over H when column blocks x pairs would leave most CUs idle.
+    const int ce_wgs = ((p.B + kCeCols - 1) / kCeCols) * p.P;
+    const int nch = p.H / kKChunk;
+    int slices = ce_wgs >= kCeTargetWorkgroups ? 1 : (kCeTargetWorkgroups + ce_wgs - 1) / ce_wgs;
+    slices = std::max(1, std::min(slices, nch / 4));
+    p.ce_kper = ((nch + slices - 1) / slices + 3) / 4 * 4;
+    p.ce_slices = (nch + p.ce_kper - 1) / p.ce_kper;
+    if (p.ce_slices > 1) p.off_zpart = region(sizeof(float) * p.ce_slices * models * p.B * kCeRows);
   } else {
     for (int l = 0; l <= p.L; ++l) {
       const std::initializer_list<TensorDesc> mats =
@@ -429,10 +443,24 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
         ce.H = p.H; ce.B = p.B; ce.V = p.V; ce.T = p.T; ce.t = t;
         ce.ncols_pad = static_cast<int>(p.ncols_pad);
         ce.tensor_wout = tw.id;
-        const double flops = 2.0 * p.V * p.H * double(ncols);
-        CDRGE_TRY(timed(ctx, 1, flops, [&] {
-          hipLaunchKernelGGL(k_logits_ce_bf16, cgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
-        }));
+        ce.kper = p.ce_kper;
+        ce.zpart = p.ce_slices > 1 ? ctx->at<float>(p.off_zpart) : nullptr;
+        const double flops = 2.0 * kCeRows * p.H * double(ncols);
+        if (p.ce_slices == 1) {
+          CDRGE_TRY(timed(ctx, 1, flops, [&] {
+            hipLaunchKernelGGL(k_logits_ce_bf16<false>, cgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
+          }));
+        } else {
+          const dim3 sgrid(cgrid.x, cgrid.y, static_cast<uint32_t>(p.ce_slices));
+          CDRGE_TRY(timed(ctx, 1, flops, [&] {
+            hipLaunchKernelGGL(k_logits_ce_bf16<true>, sgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
+          }));
+          CDRGE_TRY(timed(ctx, 1, 0.0, [&] {
+            hipLaunchKernelGGL(k_ce_reduce, dim3(static_cast<uint32_t>((ncols + 3) / 4)), dim3(256), 0, s,
+                               ctx->at<float>(p.off_zpart), p.ce_slices, ncols, p.B, p.V, p.T, t, bout_m,
+                               tokens, seq);
+          }));
+        }
       }
     }
     CDRGE_TRY(timed(ctx, 3, 0.0, [&] {

@@ -29,8 +29,14 @@ __device__ __forceinline__ uint32_t pair_mask(uint32_t word, int m) {
 // waves: (64-column half, model); each wave owns 64 x 64 = 4 x 4 MFMA tiles. The softmax over the
 // 64 rows of one column spans the 4 lane groups of a wave, reduced with cross-lane shuffles.
 // seq[m][b] accumulates sum_t (logsumexp - logit of the next token) in float, in t order.
+//
+// kSplit: when the grid (column blocks x pairs) is too small to fill the chip, the reduction over
+// H is split into gridDim.z slices of `kper` chunks; each workgroup writes its partial logits to
+// zpart[slice][column][64] and k_ce_reduce finishes the sum (in slice order), the softmax and the
+// cross-entropy.
 // ---------------------------------------------------------------------------------------------
 constexpr int kCeRows = 64;
+constexpr int kCeTargetWorkgroups = 512;  // split the reduction below this many workgroups
 constexpr size_t kCeLdsBytes =
     sizeof(uint16_t) * (2 * 2 * kCeRows * kCeLdsStride + 2 * 2 * kCeCols * kCeLdsStride);
 
@@ -42,11 +48,14 @@ struct CeArgs {
   const int32_t* tokens;   // [B][T+1]
   const uint64_t* seeds;
   float* seq;              // [2P][B]
+  float* zpart;            // split: partial logits [slices][2P B][64]
   int pair0, H, B, V, T, t, ncols_pad;
+  int kper;                // split: 32-wide chunks per slice (a multiple of 4)
   uint32_t tensor_wout;
 };
 
-// grid: (ceil(B / 128), pairs in chunk)
+// grid: (ceil(B / 128), pairs in chunk, slices)
+template <bool kSplit>
 __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* As = smem;                                  // [buf][side][64][40]
@@ -72,6 +81,8 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
     bcol_g[j] = static_cast<int64_t>(2 * pr + (n >> 7)) * a.B + (bvalid[j] ? b : 0);
   }
   const int nch = H / kKChunk;
+  const int c_begin = kSplit ? blockIdx.z * a.kper : 0;
+  const int c_end = kSplit ? min(nch, c_begin + a.kper) : nch;
   uint4 rp[4], rm[4], rb[4];
   PhiloxOut words{0, 0, 0, 0};
 
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   };
   auto form_store = [&](int c, int buf) {
     if (former) {
-      if ((c & 3) == 0)
+      if ((c & 3) == 0)  // c_begin is a multiple of 4
         words = sign_block(seed, a.tensor_wout, static_cast<uint32_t>(frow), static_cast<uint32_t>(c >> 2));
       const uint32_t w = pick_word(words, static_cast<uint32_t>(c & 3));
       const uint32_t p32[16] = {rp[0].x, rp[0].y, rp[0].z, rp[0].w, rp[1].x, rp[1].y, rp[1].z, rp[1].w,
@@ -143,19 +154,35 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
     }
   };
 
-  load(0);
-  form_store(0, 0);
+  load(c_begin);
+  form_store(c_begin, 0);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) load(c + 1);
-    mma(c & 1);
-    if (c + 1 < nch) form_store(c + 1, (c + 1) & 1);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int buf = (c - c_begin) & 1;
+    if (c + 1 < c_end) load(c + 1);
+    mma(buf);
+    if (c + 1 < c_end) form_store(c + 1, buf ^ 1);
     __syncthreads();
   }
 
   const int m = 2 * pr + side;
-  const float* bout = a.bout_m + static_cast<int64_t>(m) * kCeRows;
   const int g = lane >> 4;
+  if constexpr (kSplit) {
+    // partial logits of rows 16 i + 4 g .. + 3 for this lane's four columns
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = bcol0 + 64 * ch + 16 * j + (lane & 15);
+      if (b < a.B) {
+        float4* dst = reinterpret_cast<float4*>(
+            a.zpart + ((static_cast<int64_t>(blockIdx.z) * gridDim.y * 2 + m) * a.B + b) * kCeRows);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[4 * i + g] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+    return;
+  }
+  const float* bout = a.bout_m + static_cast<int64_t>(m) * kCeRows;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = 64 * ch + 16 * j + (lane & 15);
@@ -194,6 +221,36 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
       float* dst = a.seq + static_cast<int64_t>(m) * a.B + b;
       *dst = (a.t == 0) ? l : *dst + l;
     }
+  }
+}
+
+// Finishes the split logits: one wave per (model, sequence) column of the chunk, lane = logit
+// row. z = bout + sum over slices (in slice order) of the partials, then the softmax
+// cross-entropy against the next token, accumulated into seq[m][b] over t.
+// grid: ceil(2P B / 4) blocks of 256 threads.
+__global__ __launch_bounds__(256) void k_ce_reduce(const float* __restrict__ zpart, int slices, int ncols,
+                                                   int B, int V, int T, int t, const float* __restrict__ bout_m,
+                                                   const int32_t* __restrict__ tokens, float* __restrict__ seq) {
+  const int lane = threadIdx.x & 63;
+  const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= ncols) return;
+  const int m = col / B, b = col % B;
+  float z = bout_m[static_cast<int64_t>(m) * kCeRows + lane];
+  for (int sl = 0; sl < slices; ++sl) z += zpart[(static_cast<int64_t>(sl) * ncols + col) * kCeRows + lane];
+  const bool row_ok = lane < V;
+  float zmax = row_ok ? z : -INFINITY;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o));
+  float e = row_ok ? __expf(z - zmax) : 0.f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+  int y = tokens[static_cast<int64_t>(b) * (T + 1) + t + 1];
+  y = min(max(y, 0), V - 1);
+  const float zy = __shfl(z, y);
+  if (lane == 0) {
+    const float l = (zmax + __logf(e)) - zy;
+    float* dst = seq + static_cast<int64_t>(m) * B + b;
+    *dst = (t == 0) ? l : *dst + l;
   }
 }
 
