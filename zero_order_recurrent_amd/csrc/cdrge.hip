@@ -483,7 +483,7 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
                                         (2.0 * p.K * static_cast<double>(p.cfg.eps)));
   const bool bf16 = p.cfg.dtype == CDRGE_BF16;
   const size_t esz = bf16 ? 2 : 4;
-  if (bf16 && p.K <= kUpdLutMaxProbes && static_cast<int>(p.tensors.size()) <= kUpdMaxTensors) {
+  if (p.K <= kUpdLutMaxProbes && static_cast<int>(p.tensors.size()) <= kUpdMaxTensors) {
     // all tensors in one launch (tensor ids are their positions in the flat layout)
     UpdTensors ut{};
     int64_t segs = 0;
@@ -498,10 +498,15 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
     }
     const int64_t blocks = (segs + kUpdLutThreads / 4 - 1) / (kUpdLutThreads / 4);
     const dim3 lgrid(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096));
-    const double bytes = 2.0 * double(p.d) * 2;
+    const double bytes = 2.0 * double(p.d) * esz;
+    const int copies = update_lut_copies(p.K);
     return timed(ctx, 2, bytes, [&] {
-      hipLaunchKernelGGL(k_update_lut_bf16, lgrid, dim3(kUpdLutThreads), update_lut_bytes(p.K), s,
-                         static_cast<uint16_t*>(ctx->params), ut, seeds, losses, p.K, coef, flags);
+      if (bf16)
+        hipLaunchKernelGGL(k_update_lut<uint16_t>, lgrid, dim3(kUpdLutThreads), update_lut_bytes(p.K), s,
+                           static_cast<uint16_t*>(ctx->params), ut, seeds, losses, p.K, copies, coef, flags);
+      else
+        hipLaunchKernelGGL(k_update_lut<float>, lgrid, dim3(kUpdLutThreads), update_lut_bytes(p.K), s,
+                           static_cast<float*>(ctx->params), ut, seeds, losses, p.K, copies, coef, flags);
     });
   }
   for (const TensorDesc& t : p.tensors) {
@@ -526,15 +531,18 @@ cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   if (cfg->dtype == CDRGE_BF16) {
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_gates_bf16),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
-    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_update_lut_bf16),
+    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_update_lut<uint16_t>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  static_cast<int>(update_lut_bytes(kUpdLutMaxProbes))));
+                                  static_cast<int>(update_lut_bytes(ctx->plan.K))));
   } else {
     const Plan& p = ctx->plan;
     const int lds = static_cast<int>(
         sizeof(float) * f32_lds_layout(p.L, p.V, p.E, p.H, p.f32_g, p.f32_nb, p.f32_threads).total);
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(f32_kernel(p.f32_g, p.f32_nb)),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_update_lut<float>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(update_lut_bytes(p.K))));
   }
   uint32_t* flags = ctx->at<uint32_t>(ctx->plan.off_flags);
   hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, ctx->stream, flags, 0u);

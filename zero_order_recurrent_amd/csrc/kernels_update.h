@@ -1,5 +1,6 @@
-// Seed-regenerating CD-RGE update for bf16 parameters, with 8-probe look-up tables:
-//   theta_j <- bf16(theta_j - coef * sum_i p_i(j) d_i),   d_i = L(theta + eps p_i) - L(theta - eps p_i)
+// Seed-regenerating CD-RGE update, with 8-probe look-up tables:
+//   theta_j <- R(theta_j - coef * sum_i p_i(j) d_i),   d_i = L(theta + eps p_i) - L(theta - eps p_i),
+// R the rounding to the parameters' storage type (bf16 round-to-nearest-even, or none for fp32)
 // (the update of the pith.science review, "What carries the argument", in the eta / (2 K eps)
 // form of the alex-wiki source note, "Method"; the probes are regenerated from their seeds).
 //
@@ -23,10 +24,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kUpdLutThreads = 256;
-constexpr int kUpdLutCopies = 4;        // one table copy per 16 lanes
-constexpr int kUpdLutStride = 256 + 16; // copies 16 banks apart, so equal indices from different
-                                        // lane groups hit different banks
-constexpr int kUpdLutMaxProbes = 128;   // 16 groups x 4 copies x 1 KB of tables
+constexpr int kUpdLutStride = 256 + 16; // table copies 16 banks apart, so equal indices from
+                                        // different lane groups hit different banks
+constexpr int kUpdLutMaxProbes = 1024;
+constexpr size_t kUpdLutMaxBytes = 144 * 1024;  // dynamic LDS of the tables
 
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
@@ -35,8 +36,16 @@ __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
 }
 
+// Copies of each table (1, 2 or 4; lane group l of 16 lanes reads copy l % copies): as many as
+// fit in kUpdLutMaxBytes for K probes.
+inline int update_lut_copies(int K) {
+  const size_t one = sizeof(float) * ((K + 7) / 8) * kUpdLutStride;
+  return one * 4 <= kUpdLutMaxBytes ? 4 : (one * 2 <= kUpdLutMaxBytes ? 2 : 1);
+}
 // LDS bytes of the tables for K probes.
-inline size_t update_lut_bytes(int K) { return sizeof(float) * ((K + 7) / 8) * kUpdLutCopies * kUpdLutStride; }
+inline size_t update_lut_bytes(int K) {
+  return sizeof(float) * ((K + 7) / 8) * update_lut_copies(K) * kUpdLutStride;
+}
 
 // The tensors of the flat parameter vector, as one index space of 128-column row segments.
 constexpr int kUpdMaxTensors = 32;
@@ -47,13 +56,17 @@ struct UpdTensors {
   int n;
 };
 
-// One launch for all tensors of bf16 parameters, K <= kUpdLutMaxProbes. A quad of lanes handles
-// one 128-column segment (lane q: columns 32q .. 32q + 31); workgroups stride over the segments
-// and the parameters of the next segment are requested before the current one is computed.
-// Non-finite losses: nothing is written and flags[0] is raised.
-__global__ __launch_bounds__(kUpdLutThreads) void k_update_lut_bf16(
-    uint16_t* __restrict__ theta_all, UpdTensors tens, const uint64_t* __restrict__ seeds,
-    const float* __restrict__ losses, int K, float coef, uint32_t* __restrict__ flags) {
+// One launch for all tensors, K <= kUpdLutMaxProbes; T is uint16_t (bf16 bit patterns) or
+// float. A quad of lanes handles one 128-column segment (lane q: columns 32q .. 32q + 31);
+// workgroups stride over the segments and the parameters of the next segment are requested
+// before the current one is computed. Non-finite losses: nothing is written and flags[0] is
+// raised.
+template <typename T>
+__global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
+    T* __restrict__ theta_all, UpdTensors tens, const uint64_t* __restrict__ seeds,
+    const float* __restrict__ losses, int K, int copies, float coef, uint32_t* __restrict__ flags) {
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int kVec = 32 * sizeof(T) / 16;  // 16-byte pieces of a lane's 32 parameters
   extern __shared__ float lut[];  // [group][copy][kUpdLutStride], 256 entries used
   __shared__ uint64_t sseed[kUpdLutMaxProbes];
   __shared__ float sdif[kUpdLutMaxProbes];
@@ -87,14 +100,13 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut_bf16(
       const float dv = sdif[8 * g + k];
       t += ((m >> k) & 1) ? -dv : dv;   // sign bit set: p = -1
     }
-#pragma unroll
-    for (int cp = 0; cp < kUpdLutCopies; ++cp) lut[(g * kUpdLutCopies + cp) * kUpdLutStride + m] = t;
+    for (int cp = 0; cp < copies; ++cp) lut[(g * copies + cp) * kUpdLutStride + m] = t;
   }
   __syncthreads();
 
   const int lane = tid & 63, ell = tid & 3;
   const int odd1 = ell & 1, odd2 = (ell >> 1) & 1;
-  const float* lcopy = lut + (lane >> 4) * kUpdLutStride;
+  const float* lcopy = lut + ((lane >> 4) & (copies - 1)) * kUpdLutStride;
   // 4x4 word transpose within the quad: v[w] = word w of the block this lane evaluated becomes
   // word `ell` of the block that quad lane w evaluated.
   auto qtrans = [&](uint32_t (&v)[4]) {
@@ -113,7 +125,7 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut_bf16(
   const int64_t quads = static_cast<int64_t>(gridDim.x) * (kUpdLutThreads / 4);
   // Locates a segment: tensor id, row, 128-column block, and this lane's first element.
   struct Seg {
-    uint16_t* t;
+    T* t;
     int r, blk, c0, cols;
     uint32_t id;
     int full;
@@ -134,23 +146,23 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut_bf16(
     g.full = (g.c0 + 32 <= cols) && ((reinterpret_cast<uintptr_t>(g.t) & 15u) == 0);
     return g;
   };
-  auto load32 = [](const Seg& g, uint4 (&wv)[4]) {
+  auto load32 = [](const Seg& g, uint4 (&wv)[kVec]) {
     if (g.full) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) wv[v] = reinterpret_cast<const uint4*>(g.t)[v];
+      for (int v = 0; v < kVec; ++v) wv[v] = reinterpret_cast<const uint4*>(g.t)[v];
     }
   };
 
   int64_t seg = static_cast<int64_t>(blockIdx.x) * (kUpdLutThreads / 4) + (tid >> 2);
   if (seg >= nseg) return;
   Seg cur = locate(seg);
-  uint4 wv[4] = {};
+  uint4 wv[kVec] = {};
   load32(cur, wv);
   for (; seg < nseg; seg += quads) {
     // request the next segment's parameters first
     const int64_t nxt = seg + quads;
     Seg next = cur;
-    uint4 wn[4] = {};
+    uint4 wn[kVec] = {};
     if (nxt < nseg) {
       next = locate(nxt);
       load32(next, wn);
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut_bf16(
       swap_bits(X[2], X[3], 1, 0x55555555u);
       swap_bits(X[4], X[5], 1, 0x55555555u);
       swap_bits(X[6], X[7], 1, 0x55555555u);
-      const float* lg = lcopy + g * (kUpdLutCopies * kUpdLutStride);
+      const float* lg = lcopy + g * (copies * kUpdLutStride);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
 #pragma unroll
@@ -195,31 +207,51 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut_bf16(
     // Bit position p of the word is column 2 (p & 15) + (p >> 4): pair k of the 32 columns (16
     // 32-bit pairs) holds bit positions k (low half) and k + 16 (high half).
     if (cur.full) {
-      uint32_t in[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
-                         wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
-      uint32_t out[16];
+      if constexpr (kBf16) {
+        uint32_t in[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
+                           wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
+        uint32_t out[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float lo = __uint_as_float(in[k] << 16) - coef * acc[k];
-        const float hi = __uint_as_float(in[k] & 0xffff0000u) - coef * acc[k + 16];
-        // packed round-to-nearest-even conversion (identical to f32_to_bf16_rne for non-NaN)
-        const f32x2 v = {lo, hi};
-        out[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        for (int k = 0; k < 16; ++k) {
+          const float lo = __uint_as_float(in[k] << 16) - coef * acc[k];
+          const float hi = __uint_as_float(in[k] & 0xffff0000u) - coef * acc[k + 16];
+          // packed round-to-nearest-even conversion (identical to f32_to_bf16_rne for non-NaN)
+          const f32x2 v = {lo, hi};
+          out[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          reinterpret_cast<uint4*>(cur.t)[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
+      } else {
+        float in[32];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          in[4 * v] = __uint_as_float(wv[v].x);
+          in[4 * v + 1] = __uint_as_float(wv[v].y);
+          in[4 * v + 2] = __uint_as_float(wv[v].z);
+          in[4 * v + 3] = __uint_as_float(wv[v].w);
+        }
+#pragma unroll
+        for (int cl = 0; cl < 32; ++cl) in[cl] -= coef * acc[(cl >> 1) + ((cl & 1) << 4)];
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          reinterpret_cast<float4*>(cur.t)[v] = make_float4(in[4 * v], in[4 * v + 1], in[4 * v + 2], in[4 * v + 3]);
       }
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        reinterpret_cast<uint4*>(cur.t)[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
     } else {
 #pragma unroll
       for (int p = 0; p < 32; ++p) {
         const int cl = 2 * (p & 15) + (p >> 4);
-        if (cur.c0 + cl < cur.cols)
-          cur.t[cl] = static_cast<uint16_t>(f32_to_bf16_rne(bf16_to_f32(cur.t[cl]) - coef * acc[p]));
+        if (cur.c0 + cl < cur.cols) {
+          if constexpr (kBf16)
+            cur.t[cl] = static_cast<uint16_t>(f32_to_bf16_rne(bf16_to_f32(cur.t[cl]) - coef * acc[p]));
+          else
+            cur.t[cl] = cur.t[cl] - coef * acc[p];
+        }
       }
     }
     cur = next;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) wv[v] = wn[v];
+    for (int v = 0; v < kVec; ++v) wv[v] = wn[v];
   }
 }
 
