@@ -55,7 +55,7 @@ constexpr int kTileCols = 256;                 // batch columns per model
 constexpr int kKChunk = 32;
 constexpr int kHsStride = 40;                  // bf16 per row of the h transpose buffer
 constexpr int kAStageBytes = 2 * kTileRows * 64;   // both models' 128 x 32 bf16 tiles
-constexpr int kAStages = 4;
+constexpr int kAStages = 8;
 constexpr int kBRing = 4;                          // activation register ring (chunks)
 // Workgroups resident on one XCD at a time (one per CU) cover kGroupRows row tiles x kGroupCols
 // column blocks, so that each activation chunk is fetched into that XCD's L2 once for kGroupRows
@@ -231,29 +231,32 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     }
   };
 
-  // One K step on chunk c (c % 4 == S). Requests go out at the top: first the weight candidates
-  // of chunk c+3, then (on even c) the activations of chunks c+2 and c+3. Vector loads complete
-  // in issue order, and each stream is consumed in issue order, so this order never makes a wait
-  // for one chunk hold up a newer chunk: the weights of chunk c+3 are waited for in step c+1,
-  // after everything issued before them was needed anyway. Row groups 0-5 are multiplied, each
-  // followed by the fragment reads two groups ahead (row groups 2-7 of chunk c); chunk c+2 is
-  // selected into its stage; row groups 6-7 finish, followed by the reads of row groups 0-1 of
-  // chunk c+1. Selecting late in the step gives the weight requests more time to arrive (3-4%
-  // faster than selecting after row group 3). Past the last chunk the requests repeat the last
-  // chunk and the select fills a stage that is never multiplied.
+  // One K step on chunk c (c % 4 == S). Requests go out at the top: first the weights of chunk
+  // c+5, then (on even c) the activations of chunks c+2 and c+3. Vector loads complete in issue
+  // order, and each stream is consumed in issue order, so this order never makes a wait for one
+  // chunk hold up a newer chunk: the weights of chunk c+5 are waited for in step c+1, after
+  // everything issued before them was needed anyway. Row groups 0-5 are multiplied, each followed
+  // by the fragment reads two groups ahead (row groups 2-7 of chunk c); chunk c+4 is selected
+  // into its stage; row groups 6-7 finish, followed by the reads of row groups 0-1 of chunk c+1.
+  // Selecting late in the step gives the weight requests more time to arrive. Past the last
+  // chunk the requests repeat the last chunk and the select fills a stage that is never
+  // multiplied.
   //
-  // One barrier per step, right after the select, orders the weight ring: the select of chunk
-  // c+2 overwrites the stage of chunk c-2, whose last reads (row group 7, issued after row group
-  // 5 of step c-2 and completed before that step's barrier) every wave retired before the
-  // barrier of step c-1; the fragments of chunk c+1 are first read after row group 6 of step c,
-  // after the barrier of step c-1, which follows their select.
+  // The selected tiles live in an 8-stage ring (chunk k in stage k % 8), selected 4 chunks ahead,
+  // and a barrier follows the select only in every fourth step (S = 3). That is enough:
+  //  - the fragments of chunk c+1, selected in step c-3, are first read after row group 6 of
+  //    step c, and one of steps c-3 .. c has its barrier between the two;
+  //  - the select of chunk c+4 in step c overwrites the stage of chunk c-4, whose last reads
+  //    (row group 7, after row group 5 of step c-4) complete before the barrier of whichever of
+  //    steps c-4 .. c-1 has one.
+  // Fewer barriers let the waves drift against each other and absorb memory latency.
   uint4 w_r[2];  // weight ring: chunk k in slot k % 2
   uint32_t wd_r[2];
   auto step = [&](int c, auto S) {
     constexpr int s_ = decltype(S)::value;
     constexpr int wuse = s_ % 2, wnew = (s_ + 1) % 2;
-    const int rs = c & (kAStages - 1), rs1 = (c + 1) & (kAStages - 1), ws = (c + 2) & (kAStages - 1);
-    load_w(min(c + 3, nch - 1), w_r[wnew], wd_r[wnew]);
+    const int rs = c & (kAStages - 1), rs1 = (c + 1) & (kAStages - 1), ws = (c + 4) & (kAStages - 1);
+    load_w(min(c + 5, nch - 1), w_r[wnew], wd_r[wnew]);
     if constexpr (s_ % 2 == 0) load_b_pair(c + 2, bq[(s_ + 2) % 4], bq[(s_ + 3) % 4]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
       __builtin_amdgcn_sched_barrier(0);
       if (i == 5) {
         form_w(w_r[wuse], wd_r[wuse], ws);
-        __syncthreads();
+        if constexpr (s_ == 3) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -277,17 +280,17 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     bias_s[tid] = a.bias_m[(static_cast<int64_t>(2 * pr + sd) * a.L + a.layer) * (4 * H) + g * H + u0 + u];
   }
 
-  // Prologue: activations of chunks 0 and 1 and weight candidates of chunks 0-2 requested,
-  // chunks 0 and 1 selected into stages 0 and 1, row groups 0-1 of chunk 0 read.
+  // Prologue: activations of chunks 0 and 1 and weights of chunks 0-4 requested, chunks 0-3
+  // selected into stages 0-3, row groups 0-1 of chunk 0 read.
   {
-    uint4 w0, w1;
-    uint32_t d0, d1;
-    load_w(0, w0, d0);
-    load_w(min(1, nch - 1), w1, d1);
-    load_w(min(2, nch - 1), w_r[0], wd_r[0]);
+    uint4 wp[4];
+    uint32_t dp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_w(min(k, nch - 1), wp[k], dp[k]);
+    load_w(min(4, nch - 1), w_r[0], wd_r[0]);
     load_b_pair(0, bq[0], bq[1]);
-    form_w(w0, d0, 0);
-    form_w(w1, d1, 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) form_w(wp[k], dp[k], k);
   }
   __syncthreads();
   read_a(0, 0, afr[0]);
