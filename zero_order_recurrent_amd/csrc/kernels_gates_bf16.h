@@ -82,10 +82,14 @@ __device__ __forceinline__ void lstm_cell(float gi, float gf, float gg, float go
 }
 
 // Byte offset of 16-byte piece p (k = 8p..8p+7) of row r in a tile of 64-byte rows. Pieces are
-// XOR-swizzled with (r >> 2) & 3: the 16 lanes of one LDS phase - 16 consecutive rows at one
-// piece (fragment reads) or 4 rows x 4 pieces (select writes) - touch 16 distinct 16-byte bank
-// groups.
-__device__ __forceinline__ int piece_offset(int r, int p) { return r * 64 + 16 * (p ^ ((r >> 2) & 3)); }
+// XOR-swizzled with f(r) = ((r >> 1) ^ ((r >> 3) & 1)) & 3, which depends on r mod 16 only (a
+// fragment of 16 rows starts 1 KB further) and spreads every access pattern of the kernel over
+// distinct 16-byte bank groups whether the LDS serves 16-byte accesses 8 lanes per 128 bytes or
+// 16 lanes per 256 bytes: for one piece, rows r and r + 2 (and r, r + 4, r + 8, r + 12) get
+// different f; a select write covers 4 consecutive rows x 4 pieces.
+__device__ __forceinline__ int piece_offset(int r, int p) {
+  return r * 64 + 16 * (p ^ (((r >> 1) ^ ((r >> 3) & 1)) & 3));
+}
 
 struct GateArgs {
   const uint16_t* w_ih;    // W_ih [4H][in], bf16 parameters
