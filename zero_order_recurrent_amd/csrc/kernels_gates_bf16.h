@@ -235,11 +235,12 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     }
   };
 
-  // One K step on chunk c (c % 4 == S). Requests go out at the top: first the weights of chunk
-  // c+5, then (on even c) the activations of chunks c+2 and c+3. Vector loads complete in issue
-  // order, and each stream is consumed in issue order, so this order never makes a wait for one
-  // chunk hold up a newer chunk: the weights of chunk c+5 are waited for in step c+1, after
-  // everything issued before them was needed anyway. Row groups 0-5 are multiplied, each followed
+  // One K step on chunk c (c % 4 == S). Requests go out at the top: on odd steps the weights of
+  // chunks c+5 and c+6 (the two 64-byte halves of each row's 128-byte line, back to back, so that
+  // the L1 fetches every line once), on even steps the activations of chunks c+2 and c+3. Vector
+  // loads complete in issue order, and each stream is consumed in issue order, so this order
+  // never makes a wait for one chunk hold up a newer chunk: the weights of chunk c+5 are waited
+  // for in step c+1, after everything issued before them was needed anyway. Row groups 0-5 are multiplied, each followed
   // by the fragment reads two groups ahead (row groups 2-7 of chunk c); chunk c+4 is selected
   // into its stage; row groups 6-7 finish, followed by the reads of row groups 0-1 of chunk c+1.
   // Selecting late in the step gives the weight requests more time to arrive. Past the last
@@ -254,13 +255,16 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   //    (row group 7, after row group 5 of step c-4) complete before the barrier of whichever of
   //    steps c-4 .. c-1 has one.
   // Fewer barriers let the waves drift against each other and absorb memory latency.
-  uint4 w_r[2];  // weight ring: chunk k in slot k % 2
-  uint32_t wd_r[2];
+  uint4 w_r[4];  // weight ring: chunk k in slot k % 4
+  uint32_t wd_r[4];
   auto step = [&](int c, auto S) {
     constexpr int s_ = decltype(S)::value;
-    constexpr int wuse = s_ % 2, wnew = (s_ + 1) % 2;
+    constexpr int wuse = s_;
     const int rs = c & (kAStages - 1), rs1 = (c + 1) & (kAStages - 1), ws = (c + 4) & (kAStages - 1);
-    load_w(min(c + 5, nch - 1), w_r[wnew], wd_r[wnew]);
+    if constexpr (s_ % 2 == 1) {
+      load_w(min(c + 5, nch - 1), w_r[(s_ + 1) % 4], wd_r[(s_ + 1) % 4]);
+      load_w(min(c + 6, nch - 1), w_r[(s_ + 2) % 4], wd_r[(s_ + 2) % 4]);
+    }
     if constexpr (s_ % 2 == 0) load_b_pair(c + 2, bq[(s_ + 2) % 4], bq[(s_ + 3) % 4]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     bias_s[tid] = a.bias_m[(static_cast<int64_t>(2 * pr + sd) * a.L + a.layer) * (4 * H) + g * H + u0 + u];
   }
 
-  // Prologue: activations of chunks 0 and 1 and weights of chunks 0-4 requested, chunks 0-3
+  // Prologue: activations of chunks 0 and 1 and weights of chunks 0-5 requested, chunks 0-3
   // selected into stages 0-3, row groups 0-1 of chunk 0 read.
   {
     uint4 wp[4];
@@ -292,6 +296,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
 #pragma unroll
     for (int k = 0; k < 4; ++k) load_w(min(k, nch - 1), wp[k], dp[k]);
     load_w(min(4, nch - 1), w_r[0], wd_r[0]);
+    load_w(min(5, nch - 1), w_r[1], wd_r[1]);
     load_b_pair(0, bq[0], bq[1]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) form_w(wp[k], dp[k], k);
