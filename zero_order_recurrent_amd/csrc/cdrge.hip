@@ -388,10 +388,18 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       const int n_rt = p.H / kUnitsPerTile;
       const int n_cb = (p.B + kTileCols - 1) / kTileCols;
       const int n_blocks = n_rt * n_cb * pc;
-      // The XCD-grouped order needs whole groups of kGroupRows row tiles x kGroupCols column
-      // blocks on each of the 8 XCDs.
-      const int swizzle = (n_rt % kGroupRows == 0) && ((n_cb * pc) % kGroupCols == 0) &&
-                          (n_blocks % (8 * kGroupRows * kGroupCols) == 0);
+      // The XCD-grouped order needs whole groups of group_rows row tiles x group_cols column
+      // blocks on each of the 8 XCDs: 16 x 2 where the row tiles allow it, else 8 x 4.
+      int group_rows = 0, group_cols = 0;
+      for (const int gr : {16, 8}) {
+        const int gc = 32 / gr;
+        if (n_rt % gr == 0 && (n_cb * pc) % gc == 0 && n_blocks % (8 * gr * gc) == 0) {
+          group_rows = gr;
+          group_cols = gc;
+          break;
+        }
+      }
+      const int swizzle = group_rows > 0;
       const dim3 ggrid(n_blocks);
       const dim3 cgrid((p.B + kCeCols - 1) / kCeCols, pc);
       for (int t = 0; t < p.T; ++t) {
@@ -425,6 +433,8 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           g.n_col_blocks = n_cb;
           g.n_pairs = pc;
           g.swizzle = swizzle;
+          g.group_rows = group_rows;
+          g.group_cols = group_cols;
           const double flops = 2.0 * 4 * p.H * double(g.in + (g.first ? 0 : p.H)) * ncols;
           CDRGE_TRY(timed(ctx, 0, flops, [&] {
             hipLaunchKernelGGL(k_lstm_gates_bf16, ggrid, dim3(kGateThreads), kGateLdsBytes, s, g);

@@ -57,10 +57,10 @@ constexpr int kHsStride = 40;                  // bf16 per row of the h transpos
 constexpr int kAStageBytes = 2 * kTileRows * 64;   // both models' 128 x 32 bf16 tiles
 constexpr int kAStages = 8;
 constexpr int kBRing = 4;                          // activation register ring (chunks)
-// Workgroups resident on one XCD at a time (one per CU) cover kGroupRows row tiles x kGroupCols
-// column blocks, so that each activation chunk is fetched into that XCD's L2 once for kGroupRows
-// workgroups and each weight chunk once for kGroupCols.
-constexpr int kGroupRows = 8, kGroupCols = 4;
+// Workgroups resident on one XCD at a time (one per CU, 32 per XCD) cover group_rows row tiles x
+// group_cols column blocks (16 x 2 or 8 x 4, chosen by the host), so that each activation chunk
+// is fetched into that XCD's L2 once for group_rows workgroups and each weight chunk once for
+// group_cols.
 constexpr size_t kGateBiasOffset = size_t(kAStages) * kAStageBytes;
 constexpr size_t kGateLdsBytes = kGateBiasOffset + sizeof(float) * 2 * 4 * kUnitsPerTile;  // + gate biases
 static_assert(sizeof(uint16_t) * 2 * kTileCols * kHsStride <= kGateBiasOffset,
@@ -103,7 +103,7 @@ struct GateArgs {
   const float* bias_m;     // per-model perturbed gate bias [2P][L][4H]
   float eps;
   int in, H, B, L, layer, first, ncols_pad;
-  int n_row_tiles, n_col_blocks, n_pairs, swizzle;
+  int n_row_tiles, n_col_blocks, n_pairs, swizzle, group_rows, group_cols;
 };
 
 // Row tile / column block / pair of this workgroup (see the header comment for the XCD order).
@@ -112,14 +112,15 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
   int rtile, cw;
   if (a.swizzle) {
     // Workgroups are dealt to the 8 XCDs round-robin; v enumerates one XCD's workgroups in
-    // dispatch order, and each run of kGroupRows * kGroupCols of them covers kGroupRows row tiles
-    // x kGroupCols column blocks (the host checks the divisibility this needs).
+    // dispatch order, and each run of group_rows * group_cols of them covers group_rows row tiles
+    // x group_cols column blocks (the host checks the divisibility this needs).
     const int n = gridDim.x;
     const int v = (L & 7) * (n >> 3) + (L >> 3);
-    const int g = v / (kGroupRows * kGroupCols), q = v % (kGroupRows * kGroupCols);
-    const int n_rg = a.n_row_tiles / kGroupRows;
-    rtile = (g % n_rg) * kGroupRows + q % kGroupRows;
-    cw = (g / n_rg) * kGroupCols + q / kGroupRows;
+    const int gr = a.group_rows, gsz = a.group_rows * a.group_cols;
+    const int g = v / gsz, q = v % gsz;
+    const int n_rg = a.n_row_tiles / gr;
+    rtile = (g % n_rg) * gr + q % gr;
+    cw = (g / n_rg) * a.group_cols + q / gr;
   } else {
     rtile = L % a.n_row_tiles;
     cw = L / a.n_row_tiles;
@@ -131,7 +132,7 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
 
 __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
-  char* As = reinterpret_cast<char*>(smem);  // [4 stages][model][128 rows][64 B], swizzled
+  char* As = reinterpret_cast<char*>(smem);  // [8 stages][model][128 rows][64 B], swizzled
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
