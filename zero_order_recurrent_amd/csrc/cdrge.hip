@@ -510,13 +510,26 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
     const dim3 lgrid(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096));
     const double bytes = 2.0 * double(p.d) * esz;
     const int copies = update_lut_copies(p.K);
+    const size_t lds = update_lut_bytes(p.K);
+    void* th = ctx->params;
     return timed(ctx, 2, bytes, [&] {
-      if (bf16)
-        hipLaunchKernelGGL(k_update_lut<uint16_t>, lgrid, dim3(kUpdLutThreads), update_lut_bytes(p.K), s,
-                           static_cast<uint16_t*>(ctx->params), ut, seeds, losses, p.K, copies, coef, flags);
-      else
-        hipLaunchKernelGGL(k_update_lut<float>, lgrid, dim3(kUpdLutThreads), update_lut_bytes(p.K), s,
-                           static_cast<float*>(ctx->params), ut, seeds, losses, p.K, copies, coef, flags);
+      if (bf16) {
+        uint16_t* t = static_cast<uint16_t*>(th);
+        if (copies == 4)
+          hipLaunchKernelGGL((k_update_lut<uint16_t, 4>), lgrid, dim3(kUpdLutThreads), lds, s, t, ut, seeds, losses, p.K, coef, flags);
+        else if (copies == 2)
+          hipLaunchKernelGGL((k_update_lut<uint16_t, 2>), lgrid, dim3(kUpdLutThreads), lds, s, t, ut, seeds, losses, p.K, coef, flags);
+        else
+          hipLaunchKernelGGL((k_update_lut<uint16_t, 1>), lgrid, dim3(kUpdLutThreads), lds, s, t, ut, seeds, losses, p.K, coef, flags);
+      } else {
+        float* t = static_cast<float*>(th);
+        if (copies == 4)
+          hipLaunchKernelGGL((k_update_lut<float, 4>), lgrid, dim3(kUpdLutThreads), lds, s, t, ut, seeds, losses, p.K, coef, flags);
+        else if (copies == 2)
+          hipLaunchKernelGGL((k_update_lut<float, 2>), lgrid, dim3(kUpdLutThreads), lds, s, t, ut, seeds, losses, p.K, coef, flags);
+        else
+          hipLaunchKernelGGL((k_update_lut<float, 1>), lgrid, dim3(kUpdLutThreads), lds, s, t, ut, seeds, losses, p.K, coef, flags);
+      }
     });
   }
   for (const TensorDesc& t : p.tensors) {
@@ -536,23 +549,35 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
   return CDRGE_OK;
 }
 
+// Allows the update kernel for K probes its table LDS.
+hipError_t set_update_lds(int K, bool bf16) {
+  const int copies = update_lut_copies(K);
+  const int bytes = static_cast<int>(update_lut_bytes(K));
+  const void* f = nullptr;
+  if (bf16)
+    f = copies == 4 ? reinterpret_cast<const void*>(k_update_lut<uint16_t, 4>)
+                    : (copies == 2 ? reinterpret_cast<const void*>(k_update_lut<uint16_t, 2>)
+                                   : reinterpret_cast<const void*>(k_update_lut<uint16_t, 1>));
+  else
+    f = copies == 4 ? reinterpret_cast<const void*>(k_update_lut<float, 4>)
+                    : (copies == 2 ? reinterpret_cast<const void*>(k_update_lut<float, 2>)
+                                   : reinterpret_cast<const void*>(k_update_lut<float, 1>));
+  return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   CDRGE_HIP(hipGetDevice(&ctx->device));
   if (cfg->dtype == CDRGE_BF16) {
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_gates_bf16),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
-    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_update_lut<uint16_t>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  static_cast<int>(update_lut_bytes(ctx->plan.K))));
+    CDRGE_HIP(set_update_lds(ctx->plan.K, true));
   } else {
     const Plan& p = ctx->plan;
     const int lds = static_cast<int>(
         sizeof(float) * f32_lds_layout(p.L, p.V, p.E, p.H, p.f32_g, p.f32_nb, p.f32_threads).total);
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(f32_kernel(p.f32_g, p.f32_nb)),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_update_lut<float>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  static_cast<int>(update_lut_bytes(p.K))));
+    CDRGE_HIP(set_update_lds(ctx->plan.K, false));
   }
   uint32_t* flags = ctx->at<uint32_t>(ctx->plan.off_flags);
   hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, ctx->stream, flags, 0u);

@@ -27,7 +27,7 @@ constexpr int kUpdLutThreads = 256;
 constexpr int kUpdLutStride = 256 + 16; // table copies 16 banks apart, so equal indices from
                                         // different lane groups hit different banks
 constexpr int kUpdLutMaxProbes = 1024;
-constexpr size_t kUpdLutMaxBytes = 144 * 1024;  // dynamic LDS of the tables
+constexpr size_t kUpdLutMaxBytes = 144 * 1024;  // LDS of the tables
 
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
@@ -42,9 +42,11 @@ inline int update_lut_copies(int K) {
   const size_t one = sizeof(float) * ((K + 7) / 8) * kUpdLutStride;
   return one * 4 <= kUpdLutMaxBytes ? 4 : (one * 2 <= kUpdLutMaxBytes ? 2 : 1);
 }
-// LDS bytes of the tables for K probes.
+// Dynamic LDS bytes for K probes: the seeds and loss differences of 8 ceil(K / 8) probes, then
+// the tables.
 inline size_t update_lut_bytes(int K) {
-  return sizeof(float) * ((K + 7) / 8) * update_lut_copies(K) * kUpdLutStride;
+  const size_t kp = 8 * static_cast<size_t>((K + 7) / 8);
+  return 12 * kp + sizeof(float) * ((K + 7) / 8) * update_lut_copies(K) * kUpdLutStride;
 }
 
 // The tensors of the flat parameter vector, as one index space of 128-column row segments.
@@ -61,18 +63,20 @@ struct UpdTensors {
 // workgroups stride over the segments and the parameters of the next segment are requested
 // before the current one is computed. Non-finite losses: nothing is written and flags[0] is
 // raised.
-template <typename T>
+template <typename T, int kCopies>
 __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
     T* __restrict__ theta_all, UpdTensors tens, const uint64_t* __restrict__ seeds,
-    const float* __restrict__ losses, int K, int copies, float coef, uint32_t* __restrict__ flags) {
+    const float* __restrict__ losses, int K, float coef, uint32_t* __restrict__ flags) {
+  constexpr int copies = kCopies;
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int kVec = 32 * sizeof(T) / 16;  // 16-byte pieces of a lane's 32 parameters
-  extern __shared__ float lut[];  // [group][copy][kUpdLutStride], 256 entries used
-  __shared__ uint64_t sseed[kUpdLutMaxProbes];
-  __shared__ float sdif[kUpdLutMaxProbes];
+  extern __shared__ __align__(16) uint64_t upd_smem[];
+  const int G = (K + 7) / 8;
+  uint64_t* sseed = upd_smem;                                // [8 G]
+  float* sdif = reinterpret_cast<float*>(upd_smem + 8 * G);  // [8 G]
+  float* lut = sdif + 8 * G;  // [group][copy][kUpdLutStride], 256 entries used
   __shared__ int bad;
   const int tid = threadIdx.x;
-  const int G = (K + 7) / 8;
   if (tid == 0) bad = 0;
   __syncthreads();
   for (int i = tid; i < 8 * G; i += kUpdLutThreads) {
