@@ -28,6 +28,9 @@ SMALL = {
     "bf16_v64": b.make_config(3, 64, 96, 192, 130, 2, 2, "bf16", 1e-3, 1e-3, 81),
     # H = 416 (13 chunks of 32): the logits' reduction over H is split in two slices (8 + 5 chunks)
     "bf16_ce_split": b.make_config(1, 50, 32, 416, 40, 3, 2, "bf16", 1e-4, 1e-4, 84),
+    # smallest shapes: one sequence, one step, one probe pair, a single 32-wide K chunk per layer
+    "bf16_min": b.make_config(1, 2, 32, 32, 1, 1, 1, "bf16", 1e-2, 1e-2, 85),
+    "f32_min": b.make_config(1, 2, 1, 1, 1, 1, 1, "f32", 1e-2, 1e-2, 86),
 }
 
 
@@ -105,10 +108,12 @@ def test_signs_bit_exact_through_update(oracle, dtype):
             run.close()
 
 
+# K = 24, 300 and 600 keep 4, 2 and 1 copies of the update's probe-group tables in LDS.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_update_parity_identical_losses(oracle, dtype):
-    c = b.make_config(2, 50, 64, 192, 3, 2, 24, dtype, 1e-3, 1e-3, 99)
-    say(f"[gpu] update parity {dtype}")
+@pytest.mark.parametrize("n_probes", [24, 300, 600])
+def test_update_parity_identical_losses(oracle, dtype, n_probes):
+    c = b.make_config(2, 50, 64, 192, 3, 2, n_probes, dtype, 1e-3, 1e-3, 99)
+    say(f"[gpu] update parity {dtype} K={n_probes}")
     theta, tokens = _inputs(c, 9)
     rng = np.random.default_rng(4)
     losses = (3.0 + 1e-3 * rng.standard_normal(2 * c.n_probes)).astype(np.float32)
@@ -124,6 +129,26 @@ def test_update_parity_identical_losses(oracle, dtype):
         assert_theta_close(oracle, c, got, ref, 2e-2)
         assert np.mean(got != ref) < 1e-3
     run.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_signs_bit_exact_through_update_many_probes(oracle, dtype):
+    # K = 512 (coef = 2^-10): one table copy per group; sampled probes, first and last groups.
+    c = b.make_config(1, 50, 64, 128, 3, 2, 512, dtype, 1e-3, 1e-3, 4343)
+    say(f"[gpu] sign observation, K=512, {dtype}")
+    d = b.cdrge_param_count(c)
+    zero = np.zeros(d, np.float32 if dtype == "f32" else np.uint16)
+    tokens = np.zeros((3, 3), np.int32)
+    for i in (0, 7, 8, 263, 511):
+        run = GpuRun(c, zero, tokens)
+        losses = np.zeros(2 * c.n_probes, np.float32)
+        losses[2 * i] = 1.0
+        assert run.update(1, losses) == 0
+        got = run.theta()
+        vals = got if dtype == "f32" else (got.astype(np.uint32) << 16).view(np.float32)
+        p = oracle.probe_vector(ocfg(c), oracle.probe_seed(c.base_seed, 1, i))
+        np.testing.assert_array_equal(vals, (-p / (2 * c.n_probes)).astype(np.float32))
+        run.close()
 
 
 def test_nonfinite_loss_leaves_theta(oracle):
