@@ -13,11 +13,20 @@
 //
 // Work split. A thread owns one weight row (a gate row, or a logit row and a slice of its
 // columns) and computes that row's dot products for all 2G*NB (model, sequence) slots of the
-// workgroup, so each weight is loaded once for 2G models and its two perturbed values w +- eps
-// are formed once per pair. Weights are read from per-step k-major copies W^T (lanes hold
-// consecutive rows, so every load is coalesced) and the sign bits from per-chunk tables of
-// Philox words, one word per (pair, row, 32 columns), also row-fastest. Activations live in LDS
-// as [k][slot], so a single broadcast read returns the inputs of every slot for one k.
+// workgroup, so each weight is loaded once for 2G models. Weights are read from per-step k-major
+// copies W^T (lanes hold consecutive rows, so every load is coalesced) and the sign bits from
+// per-chunk tables of Philox words, one word per (pair, row, 32 columns), also row-fastest.
+// Activations live in LDS as [k][slot], so a single broadcast read returns the inputs of every
+// slot for one k.
+//
+// Gate rows use the identity (W + s eps P) x = W x + s eps (P x): the W x part is plain FMAs
+// shared by both models of a pair, and P x comes from tables of signed partial sums: for every
+// slot and every group of 4 columns that one nibble of a sign word covers, the 16 sums
+// +-x_a +-x_b +-x_c +-x_d are built once per timestep and layer in LDS, and a row adds the entry
+// its nibble selects. That is a quarter of a table read per column and slot instead of forming
+// w + eps and w - eps per column and pair, about half the arithmetic. The result differs from
+// summing fl(w +- eps) x only in rounding (the perturbed weight is not rounded to float before
+// the product).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,7 +76,7 @@ struct F32Args {
 
 // Offsets (in floats) of the LDS regions; every region starts on a 16-byte boundary.
 struct F32Lds {
-  int h, c, xin, gbuf, bias, bout, z, loss, total;
+  int h, c, xin, gbuf, bias, bout, z, loss, tab, tab_h, total;
 };
 __host__ __device__ inline int f32_pad4(int x) { return (x + 3) & ~3; }
 __host__ __device__ inline F32Lds f32_lds_layout(int L, int V, int E, int H, int G, int NB, int NT) {
@@ -83,6 +92,10 @@ __host__ __device__ inline F32Lds f32_lds_layout(int L, int V, int E, int H, int
   o.bout = at; at += f32_pad4(V * 2 * G);                 // [V][2G]
   o.z = at;    at += f32_pad4(V * M);                     // [V][M]
   o.loss = at; at += f32_pad4(M);                         // [M]
+  // signed partial sums of the layer input and of h: [word][nibble][slot][16]
+  const int wx = (E > H ? E : H) + 31 >> 5, wh = (H + 31) >> 5;
+  o.tab = at;  at += wx * 8 * M * 16;
+  o.tab_h = at; at += wh * 8 * M * 16;
   o.total = at;
   return o;
 }
@@ -138,13 +151,39 @@ __device__ __forceinline__ void f32_column(float (&acc)[2 * G * NB], float w, co
   }
 }
 
-// acc[slot] += sum_k (W[r][k] +- eps p(r, k)) x[k][slot] for k in [0, K): wt is W^T with `ld`
-// rows per column (wt[k * ld + r] = W[r][k]), sg the tensor's sign table with `ld` rows, x the
-// activations in LDS as [K][M]. Columns go in ascending order.
+// Tables of signed partial sums of x ([K][M] in LDS) for the nibbles of the sign words:
+// tab[((w * 8 + j) * M + s) * 16 + m] = sum over i < 4 of (bit i of m ? -x : x)[col_i][s], where
+// col_i is the column of bit position 4 j + i of word w (2 (p & 15) + (p >> 4) for p = 4 j + i);
+// columns at or past K count as zero.
+template <int M>
+__device__ __forceinline__ void f32_build_tables(const float* x, int K, float* tab, int tid, int NT) {
+  const int nw = (K + 31) >> 5;
+  for (int i = tid; i < nw * 8 * M; i += NT) {
+    const int sl = i % M, wj = i / M, j = wj & 7, w = wj >> 3;
+    float v[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int p = 4 * j + ii;
+      const int col = 32 * w + 2 * (p & 15) + (p >> 4);
+      v[ii] = col < K ? x[col * M + sl] : 0.f;
+    }
+    // bits 0, 1 of m select the signs of v0, v1; bits 2, 3 those of v2, v3
+    const float lo[4] = {v[0] + v[1], v[1] - v[0], v[0] - v[1], -v[0] - v[1]};
+    const float hi[4] = {v[2] + v[3], v[3] - v[2], v[2] - v[3], -v[2] - v[3]};
+    float4* dst = reinterpret_cast<float4*>(tab + static_cast<int64_t>(i) * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_float4(lo[0] + hi[q], lo[1] + hi[q], lo[2] + hi[q], lo[3] + hi[q]);
+  }
+}
+
+// accw[slot] += sum_k W[r][k] x[k][slot] and accp[slot] += sum_k p(r, k) x[k][slot] for
+// k in [0, K), from W^T (wt[k * ld + r] = W[r][k]), the tensor's sign table with `ld` rows, the
+// activations x ([K][M] in LDS) and their tables (f32_build_tables).
 template <int G, int NB>
-__device__ __forceinline__ void f32_row_dot(float (&acc)[2 * G * NB], const float* __restrict__ wt,
-                                            const uint32_t* __restrict__ sg, int ld, int r, int K,
-                                            const float* x, const int (&qg)[G], float eps) {
+__device__ __forceinline__ void f32_row_dot_split(float (&accw)[2 * G * NB], float (&accp)[2 * G * NB],
+                                                  const float* __restrict__ wt, const uint32_t* __restrict__ sg,
+                                                  int ld, int r, int K, const float* x, const float* tab,
+                                                  const int (&qg)[G]) {
   constexpr int M = 2 * G * NB;
   const int nw = (K + 31) >> 5;
   for (int kw = 0; kw < nw; ++kw) {
@@ -152,17 +191,27 @@ __device__ __forceinline__ void f32_row_dot(float (&acc)[2 * G * NB], const floa
 #pragma unroll
     for (int g = 0; g < G; ++g) word[g] = (sg + (static_cast<int64_t>(qg[g]) * nw + kw) * ld)[r];
     const int k0 = 32 * kw;
+    auto column = [&](int k) {
+      const float w = (wt + static_cast<int64_t>(k) * ld)[r];
+      float xv[M];
+      f32_load_slots<M>(x + k * M, xv);
+#pragma unroll
+      for (int i = 0; i < M; ++i) accw[i] = fmaf(w, xv[i], accw[i]);
+    };
     if (k0 + 32 <= K) {
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        const int k = k0 + kk;
-        const float w = (wt + static_cast<int64_t>(k) * ld)[r];
-        f32_column<G, NB>(acc, w, x + k * M, word, static_cast<uint32_t>((kk >> 1) | ((kk & 1) << 4)), eps);
-      }
+      for (int kk = 0; kk < 32; ++kk) column(k0 + kk);
     } else {
-      for (int k = k0; k < K; ++k) {
-        const float w = (wt + static_cast<int64_t>(k) * ld)[r];
-        f32_column<G, NB>(acc, w, x + k * M, word, sign_bit_pos(static_cast<uint32_t>(k)), eps);
+      for (int k = k0; k < K; ++k) column(k);
+    }
+    const float* tw = tab + kw * 8 * M * 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t nib = (word[g] >> (4 * j)) & 15u;
+#pragma unroll
+        for (int i = 2 * g * NB; i < 2 * (g + 1) * NB; ++i) accp[i] += tw[(j * M + i) * 16 + nib];
       }
     }
   }
@@ -187,6 +236,8 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
   float* bout = lds + lay.bout;
   float* z = lds + lay.z;
   float* loss = lds + lay.loss;
+  float* tab = lds + lay.tab;
+  float* tab_h = lds + lay.tab_h;
 
   const int q0 = blockIdx.x * G;
   const int b0 = blockIdx.y * NB;
@@ -248,15 +299,22 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
       const int in = (l == 0) ? E : H;
       const float* x = (l == 0) ? xin : h + (l - 1) * H * M;
       const float* hl = h + l * H * M;
+      f32_build_tables<M>(x, in, tab, tid, NT);
+      if (t > 0) f32_build_tables<M>(hl, H, tab_h, tid, NT);
+      __syncthreads();
       for (int r = tid; r < G4; r += NT) {
+        float accw[M], accp[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) accw[i] = accp[i] = 0.f;
+        f32_row_dot_split<G, NB>(accw, accp, a.wt_ih[l], a.sg_ih[l], G4, r, in, x, tab, qg);
+        if (t > 0) f32_row_dot_split<G, NB>(accw, accp, a.wt_hh[l], a.sg_hh[l], G4, r, H, hl, tab_h, qg);
+        const float* bs = bias + (l * G4 + r) * 2 * G;
         float acc[M];
 #pragma unroll
-        for (int i = 0; i < M; ++i) acc[i] = 0.f;
-        f32_row_dot<G, NB>(acc, a.wt_ih[l], a.sg_ih[l], G4, r, in, x, qg, a.eps);
-        if (t > 0) f32_row_dot<G, NB>(acc, a.wt_hh[l], a.sg_hh[l], G4, r, H, hl, qg, a.eps);
-        const float* bs = bias + (l * G4 + r) * 2 * G;
-#pragma unroll
-        for (int i = 0; i < M; ++i) acc[i] += bs[i / NB];
+        for (int i = 0; i < M; ++i) {
+          const float se = ((i / NB) & 1) ? -a.eps : a.eps;  // +eps model: w + s eps; -eps model: w - s eps
+          acc[i] = fmaf(se, accp[i], accw[i]) + bs[i / NB];
+        }
         f32_store_slots<M>(gbuf + r * M, acc);
       }
       __syncthreads();
