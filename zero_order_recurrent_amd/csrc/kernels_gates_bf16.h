@@ -11,7 +11,7 @@
 // one row, forms both candidates bf16(w + eps) and bf16(w - eps) in registers (one float add each
 // and the packed round-to-nearest-even conversion), and the probe's sign bit picks one candidate
 // per model: the +eps model takes the one the sign selects, the -eps model the other. The result
-// goes to LDS. Sign bits come from per-step tables of Philox words (one 32-bit word per row and
+// goes to LDS. Sign bits come from per-chunk tables of Philox words (one 32-bit word per row and
 // 32-column chunk, chunk-major), so both models of a pair share one weight load and one sign
 // word.
 //
@@ -22,17 +22,19 @@
 //   waves   (model, column quarter): each wave owns 128 x 64 = 8 x 4 MFMA 16x16x32 tiles
 //           (128 accumulator registers per lane).
 // K loop over the concatenated reduction [x_t ; h_{t-1}] in chunks of 32, software-pipelined:
-//   * activations go straight from global memory into the MFMA operand registers of the wave
-//     that uses them (each column belongs to one wave), in a 4-deep register ring, two chunks at
-//     a time so that both 64-byte halves of a 128-byte line are requested back to back;
-//   * the stored weights and sign words of chunk c+3 are requested at the top of step c into a
-//     2-slot register ring, and selected into LDS in step c+1;
-//   * the selected tiles of both models live in a 4-stage LDS ring; fragments are read two row
-//     groups ahead of the MFMAs that use them; one barrier per chunk, right after the select.
+//   * activations (stored k-chunk-major, so a 16-column fragment is 1 KB of contiguous memory)
+//     go straight from global memory into the MFMA operand registers of the wave that uses them
+//     (each column belongs to one wave), in a 4-deep register ring, two chunks ahead;
+//   * the stored weights and sign words of chunks c+5 and c+6 are requested together in odd
+//     steps (both halves of each row's 128-byte line back to back) into a register ring, and
+//     chunk c+4 is selected into LDS in step c, after row group 5;
+//   * the selected tiles of both models live in an 8-stage LDS ring; fragments are read two row
+//     groups ahead of the MFMAs that use them; a barrier follows the select in every fourth step.
 // The cell state stays in accumulator order (tile-private, 16 bytes per lane and row group), and
 // h leaves through an LDS transpose as whole 64-byte column segments.
-// The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 8 row
-// tiles x 4 column blocks, which keeps their shared weight and activation chunks in that XCD's L2.
+// The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 16 row
+// tiles x 2 column blocks (or 8 x 4), which keeps their shared weight and activation chunks in
+// that XCD's L2.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
