@@ -24,7 +24,7 @@
 // K loop over the concatenated reduction [x_t ; h_{t-1}] in chunks of 32, software-pipelined:
 //   * activations (stored k-chunk-major, so a 16-column fragment is 1 KB of contiguous memory)
 //     go straight from global memory into the MFMA operand registers of the wave that uses them
-//     (each column belongs to one wave), in a 4-deep register ring, two chunks ahead;
+//     (each column belongs to one wave), in a 4-deep register ring, three chunks ahead;
 //   * the stored weights and sign words of chunks c+5 and c+6 are requested together in odd
 //     steps (both halves of each row's 128-byte line back to back) into a register ring, and
 //     chunk c+4 is selected into LDS in step c, after row group 5;
@@ -224,26 +224,23 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[j], acc[i][j], 0, 0, 0);
   };
-  // Activations of chunks c and c+1 (c even): fragment j of a chunk is the 16 columns
+  // Activations of chunk c (clamped to the last one): fragment j is the 16 columns
   // 16 j .. 16 j + 15 of the wave, 512 elements further per fragment.
-  auto load_b_pair = [&](int c, bf16x8 (&d0)[4], bf16x8 (&d1)[4]) {
-    const int c0 = min(c, nch - 1), c1 = min(c + 1, nch - 1);
-    const bool x0p = c0 < kx, x1p = c1 < kx;
+  auto load_b = [&](int c, bf16x8 (&d0)[4]) {
+    const int c0 = min(c, nch - 1);
+    const bool x0p = c0 < kx;
     const uint16_t* s0 = (x0p ? a.x_in : a.h_prev) + chunk_stride * (x0p ? c0 : c0 - kx);
-    const uint16_t* s1 = (x1p ? a.x_in : a.h_prev) + chunk_stride * (x1p ? c1 : c1 - kx);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      d0[j] = *reinterpret_cast<const bf16x8*>(s0 + 16 * kKChunk * j + boff);
-      d1[j] = *reinterpret_cast<const bf16x8*>(s1 + 16 * kKChunk * j + boff);
-    }
+    for (int j = 0; j < 4; ++j) d0[j] = *reinterpret_cast<const bf16x8*>(s0 + 16 * kKChunk * j + boff);
   };
 
   // One K step on chunk c (c % 4 == S). Requests go out at the top: on odd steps the weights of
   // chunks c+5 and c+6 (the two 64-byte halves of each row's 128-byte line, back to back, so that
-  // the L1 fetches every line once), on even steps the activations of chunks c+2 and c+3. Vector
-  // loads complete in issue order, and each stream is consumed in issue order, so this order
-  // never makes a wait for one chunk hold up a newer chunk: the weights of chunk c+5 are waited
-  // for in step c+1, after everything issued before them was needed anyway. Row groups 0-5 are multiplied, each followed
+  // the L1 fetches every line once), then in every step the activations of chunk c+3 (one chunk
+  // per step keeps the request stream even). Vector loads complete in issue order, and each
+  // stream is consumed in issue order, so this order never makes a wait for one chunk hold up a
+  // newer chunk: the weights of chunk c+5 are waited for in step c+1, after everything issued
+  // before them was needed anyway. Row groups 0-5 are multiplied, each followed
   // by the fragment reads two groups ahead (row groups 2-7 of chunk c); chunk c+4 is selected
   // into its stage; row groups 6-7 finish, followed by the reads of row groups 0-1 of chunk c+1.
   // Selecting late in the step gives the weight requests more time to arrive. Past the last
@@ -268,7 +265,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
       load_w(min(c + 5, nch - 1), w_r[(s_ + 1) % 4], wd_r[(s_ + 1) % 4]);
       load_w(min(c + 6, nch - 1), w_r[(s_ + 2) % 4], wd_r[(s_ + 2) % 4]);
     }
-    if constexpr (s_ % 2 == 0) load_b_pair(c + 2, bq[(s_ + 2) % 4], bq[(s_ + 3) % 4]);
+    load_b(c + 3, bq[(s_ + 3) % 4]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -291,7 +288,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     bias_s[tid] = a.bias_m[(static_cast<int64_t>(2 * pr + sd) * a.L + a.layer) * (4 * H) + g * H + u0 + u];
   }
 
-  // Prologue: activations of chunks 0 and 1 and weights of chunks 0-5 requested, chunks 0-3
+  // Prologue: activations of chunks 0-2 and weights of chunks 0-5 requested, chunks 0-3
   // selected into stages 0-3, row groups 0-1 of chunk 0 read.
   {
     uint4 wp[4];
@@ -300,7 +297,9 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     for (int k = 0; k < 4; ++k) load_w(min(k, nch - 1), wp[k], dp[k]);
     load_w(min(4, nch - 1), w_r[0], wd_r[0]);
     load_w(min(5, nch - 1), w_r[1], wd_r[1]);
-    load_b_pair(0, bq[0], bq[1]);
+    load_b(0, bq[0]);
+    load_b(1, bq[1]);
+    load_b(2, bq[2]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) form_w(wp[k], dp[k], k);
   }
