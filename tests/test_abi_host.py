@@ -86,6 +86,16 @@ def test_workspace_plan(lib):
     assert b.cdrge_workspace_bytes(c1) < b.cdrge_workspace_bytes(c2)
 
 
+def test_workspace_flat_in_sequence_length(lib):
+    # The forward streams over t with a fixed recurrent state, so device memory does not grow
+    # with the context length (the pages' point that CD-RGE memory is flat in sequence length,
+    # unlike backpropagation through time).
+    for name in ("charlm", "lstm270m", "tiny", "overfit"):
+        p = PRESETS[name]
+        sizes = {b.cdrge_workspace_bytes(b.config_from_preset(p.with_(seq_len=T))) for T in (1, 10, 100, 10000)}
+        assert len(sizes) == 1, (name, sizes)
+
+
 def test_status_strings(lib):
     for k, v in b.STATUS.items():
         assert b.cdrge_status_string(k) == v

@@ -31,6 +31,8 @@ SMALL = {
     # smallest shapes: one sequence, one step, one probe pair, a single 32-wide K chunk per layer
     "bf16_min": b.make_config(1, 2, 32, 32, 1, 1, 1, "bf16", 1e-2, 1e-2, 85),
     "f32_min": b.make_config(1, 2, 1, 1, 1, 1, 1, "f32", 1e-2, 1e-2, 86),
+    # a long sequence: 64 steps through the same fixed-size state
+    "bf16_long": b.make_config(2, 50, 64, 128, 24, 64, 2, "bf16", 1e-4, 1e-4, 87),
 }
 
 

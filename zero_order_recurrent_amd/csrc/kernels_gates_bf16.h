@@ -344,7 +344,10 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
       const int cl = 64 * cq + 16 * j + (lane & 15);
       float hv;
       lstm_cell(acc[i][j][0] + bi, acc[i][j][1] + bf, acc[i][j][2] + bg, acc[i][j][3] + bo, cprev[j], cn[j], hv);
-      Hs[(256 * side + cl) * kHsStride + ul] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+      // hardware round-to-nearest-even conversion (equal to f32_to_bf16_rne except for NaN payloads)
+      const f32x2 hp = {hv, hv};
+      Hs[(256 * side + cl) * kHsStride + ul] =
+          static_cast<uint16_t>(__builtin_bit_cast(uint32_t, __builtin_convertvector(hp, bf16x2)));
     }
     cptr[64 * i] = make_float4(cn[0], cn[1], cn[2], cn[3]);
   }
