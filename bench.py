@@ -109,8 +109,8 @@ def main():
         print(json.dumps({"copy_bytes_per_direction": n * 4, "copies": 3}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (probe sharding across GPUs "
-              "is a design note only). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (sharding the probes across GPUs "
+              "is described, not built). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -44,7 +44,7 @@ def as_f64(theta: np.ndarray) -> np.ndarray:
     return theta.astype(np.float64)
 
 
-class GpuRun:
+class HipRun:
     def __init__(self, cfg: b.cdrge_config, theta: np.ndarray, tokens: np.ndarray):
         import torch
         self.cfg = cfg

@@ -8,7 +8,7 @@ sample of parameters from every tensor, feeding the GPU's losses to the oracle's
 import numpy as np
 import pytest
 
-from gpu_util import GpuRun, TOL, as_f64, assert_losses_close, ocfg, say
+from gpu_util import HipRun, TOL, as_f64, assert_losses_close, ocfg, say
 from zero_order_recurrent_amd import binding as b
 from zero_order_recurrent_amd.inputs import PRESETS, make_theta, make_tokens
 
@@ -33,7 +33,7 @@ def _check(oracle, name, probes, seqs):
     say(f"[gpu] full-size {name}: probes {probes} sequences {seqs}")
     d = b.cdrge_param_count(c)
     theta, tokens = make_theta(p, d), make_tokens(p)
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     losses, seq, st = run.probe_losses(0)
     assert st == 0
     assert np.isfinite(losses).all()

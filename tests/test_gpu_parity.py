@@ -9,7 +9,7 @@ inputs that are not a multiple of 32 columns. Bars: probe seeds and signs bit-ex
 import numpy as np
 import pytest
 
-from gpu_util import GpuRun, TOL, assert_losses_close, assert_theta_close, dtype_name, ocfg, say
+from gpu_util import HipRun, TOL, assert_losses_close, assert_theta_close, dtype_name, ocfg, say
 from zero_order_recurrent_amd import binding as b
 from zero_order_recurrent_amd.inputs import PRESETS, make_theta, make_tokens, to_bf16_bits
 
@@ -53,7 +53,7 @@ def test_small_step_parity(oracle, name):
     say(f"[gpu] small parity {name}")
     theta, tokens = _inputs(c, 5)
     tol = TOL[dtype_name(c)]
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     losses, seq, st = run.probe_losses(step=2)
     assert st == 0
     oc = ocfg(c)
@@ -75,7 +75,7 @@ def test_tiny_three_steps(oracle):
     say("[gpu] tiny preset, 3 steps")
     d = b.cdrge_param_count(c)
     theta, tokens = make_theta(p, d), make_tokens(p)
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     ref = theta.copy()
     oc = ocfg(c)
     for s in range(p.steps):
@@ -99,7 +99,7 @@ def test_signs_bit_exact_through_update(oracle, dtype):
     tokens = np.zeros((3, 3), np.int32)
     for step in (0, 5):
         for i in range(c.n_probes):
-            run = GpuRun(c, zero, tokens)
+            run = HipRun(c, zero, tokens)
             losses = np.zeros(2 * c.n_probes, np.float32)
             losses[2 * i] = 1.0
             assert run.update(step, losses) == 0
@@ -119,7 +119,7 @@ def test_update_parity_identical_losses(oracle, dtype, n_probes):
     theta, tokens = _inputs(c, 9)
     rng = np.random.default_rng(4)
     losses = (3.0 + 1e-3 * rng.standard_normal(2 * c.n_probes)).astype(np.float32)
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     assert run.update(3, losses) == 0
     ref = theta.copy()
     assert oracle.update(ocfg(c), ref, 3, losses) == 0
@@ -142,7 +142,7 @@ def test_signs_bit_exact_through_update_many_probes(oracle, dtype):
     zero = np.zeros(d, np.float32 if dtype == "f32" else np.uint16)
     tokens = np.zeros((3, 3), np.int32)
     for i in (0, 7, 8, 263, 511):
-        run = GpuRun(c, zero, tokens)
+        run = HipRun(c, zero, tokens)
         losses = np.zeros(2 * c.n_probes, np.float32)
         losses[2 * i] = 1.0
         assert run.update(1, losses) == 0
@@ -159,7 +159,7 @@ def test_nonfinite_loss_leaves_theta(oracle):
     theta, tokens = _inputs(c, 6)
     bad = theta.copy()
     bad[100] = 0x7FC0  # NaN in the embedding
-    run = GpuRun(c, bad, tokens)
+    run = HipRun(c, bad, tokens)
     losses, _, st = run.probe_losses(0)
     assert st == 0
     assert np.isnan(losses).any()
@@ -174,7 +174,7 @@ def test_invalid_tokens_give_nan_losses():
     say("[gpu] invalid tokens")
     theta, tokens = _inputs(c, 7)
     tokens[3, 2] = c.vocab
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     losses, _, st = run.probe_losses(0)
     assert np.isnan(losses).all()
     assert run.update(0) == 5
@@ -191,7 +191,7 @@ def test_deterministic_and_chunk_invariant(name):
     for ppc in (0, 1, 2, 0):
         cc = b.make_config(c.n_layers, c.vocab, c.embed, c.hidden, c.batch, c.seq_len, c.n_probes,
                            dtype_name(c), c.eps, c.lr, c.base_seed, probes_per_chunk=ppc)
-        run = GpuRun(cc, theta, tokens)
+        run = HipRun(cc, theta, tokens)
         losses, seq, st = run.probe_losses(1)
         assert st == 0
         outs.append((losses, seq))
@@ -205,19 +205,19 @@ def test_resume_equals_uninterrupted():
     c = SMALL["bf16_ragged"]
     say("[gpu] resume")
     theta, tokens = _inputs(c, 10)
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     for s in range(3):
         run.probe_losses(s)
         run.update(s)
     straight = run.theta()
     run.close()
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     for s in range(2):
         run.probe_losses(s)
         run.update(s)
     saved = run.theta()
     run.close()
-    run = GpuRun(c, saved, tokens)
+    run = HipRun(c, saved, tokens)
     run.probe_losses(2)
     run.update(2)
     np.testing.assert_array_equal(run.theta(), straight)
@@ -231,7 +231,7 @@ def test_xcd_grouped_tile_order(oracle, hidden, pairs):
     c = b.make_config(1, 50, 64, hidden, 256, 2, pairs, "bf16", 1e-3, 1e-3, 82)
     say(f"[gpu] xcd-grouped tile order, H={hidden}")
     theta, tokens = _inputs(c, 12)
-    run = GpuRun(c, theta, tokens)
+    run = HipRun(c, theta, tokens)
     losses, seq, st = run.probe_losses(0)
     assert st == 0
     probes, seqs = [0, 13, pairs - 1], [0, 1, 100, 255]
