@@ -194,7 +194,8 @@ def main():
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "launches": gate_n, "mean_launch_ms": gate_mean_s * 1e3,
                      "flops_per_launch": gate_flops_per_launch},
-        "update_roofline": {"bound": "hbm", "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+        "update_roofline": {"bound": "hbm", "kernel": "k_update_perm" if p.dtype == "bf16" and p.n_probes <= 64
+                            else "k_update_lut", "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
                             "frac": upd_gbs / PEAK["hbm_gbs"], "traffic": upd_traffic, "launches": upd_n,
                             "total_ms_per_step": upd_ms / args.steps},
         "time_split_ms_per_step": {"gates": gate_ms / args.steps, "logits_ce": ce_ms / args.steps,

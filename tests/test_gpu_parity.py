@@ -9,7 +9,7 @@ inputs that are not a multiple of 32 columns. Bars: probe seeds and signs bit-ex
 import numpy as np
 import pytest
 
-from gpu_util import HipRun, TOL, assert_losses_close, assert_theta_close, dtype_name, ocfg, say
+from gpu_util import HipRun, TOL, as_f64, assert_losses_close, assert_theta_close, dtype_name, ocfg, say
 from zero_order_recurrent_amd import binding as b
 from zero_order_recurrent_amd.inputs import PRESETS, make_theta, make_tokens, to_bf16_bits
 
@@ -110,9 +110,11 @@ def test_signs_bit_exact_through_update(oracle, dtype):
             run.close()
 
 
-# K = 24, 300 and 600 keep 4, 2 and 1 copies of the update's probe-group tables in LDS.
+# bf16 with K <= 64 runs the permute-addressed update: K = 8, 24, 40 and 64 give 1, 3, 5 and 8
+# probe groups in 32, 32, 16 and 16 table copies (one or two 64 KB regions). Otherwise K = 24, 300
+# and 600 keep 4, 2 and 1 copies of the probe-group tables in LDS.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n_probes", [24, 300, 600])
+@pytest.mark.parametrize("n_probes", [8, 24, 40, 64, 300, 600])
 def test_update_parity_identical_losses(oracle, dtype, n_probes):
     c = b.make_config(2, 50, 64, 192, 3, 2, n_probes, dtype, 1e-3, 1e-3, 99)
     say(f"[gpu] update parity {dtype} K={n_probes}")
@@ -133,15 +135,18 @@ def test_update_parity_identical_losses(oracle, dtype, n_probes):
     run.close()
 
 
+# K = 512 (coef = 2^-10): one table copy per group. K = 64 (coef = 2^-7): for bf16, eight probe
+# groups of the permute-addressed update in two 64 KB table regions. Sampled probes from the first,
+# a middle and the last group.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_signs_bit_exact_through_update_many_probes(oracle, dtype):
-    # K = 512 (coef = 2^-10): one table copy per group; sampled probes, first and last groups.
-    c = b.make_config(1, 50, 64, 128, 3, 2, 512, dtype, 1e-3, 1e-3, 4343)
-    say(f"[gpu] sign observation, K=512, {dtype}")
+@pytest.mark.parametrize("n_probes,probes", [(512, (0, 7, 8, 263, 511)), (64, (0, 9, 34, 56, 63))])
+def test_signs_bit_exact_through_update_many_probes(oracle, dtype, n_probes, probes):
+    c = b.make_config(1, 50, 64, 128, 3, 2, n_probes, dtype, 1e-3, 1e-3, 4343)
+    say(f"[gpu] sign observation, K={n_probes}, {dtype}")
     d = b.cdrge_param_count(c)
     zero = np.zeros(d, np.float32 if dtype == "f32" else np.uint16)
     tokens = np.zeros((3, 3), np.int32)
-    for i in (0, 7, 8, 263, 511):
+    for i in probes:
         run = HipRun(c, zero, tokens)
         losses = np.zeros(2 * c.n_probes, np.float32)
         losses[2 * i] = 1.0
@@ -151,6 +156,33 @@ def test_signs_bit_exact_through_update_many_probes(oracle, dtype):
         p = oracle.probe_vector(ocfg(c), oracle.probe_seed(c.base_seed, 1, i))
         np.testing.assert_array_equal(vals, (-p / (2 * c.n_probes)).astype(np.float32))
         run.close()
+
+
+def test_update_many_segments(oracle):
+    # bf16, K = 16, d = 16.1M: each update workgroup strides over the 128-column segments several
+    # times (both parameter buffers in turn, and a partial last pass); W_ih has 1,056 columns, so
+    # every row ends in a 32-column segment. Checked on sampled elements of every tensor.
+    c = b.make_config(1, 50, 1056, 1536, 2, 2, 16, "bf16", 1e-4, 1e-4, 4444)
+    say("[gpu] update over many segments, K=16, bf16")
+    theta, tokens = _inputs(c, 11)
+    rng = np.random.default_rng(5)
+    losses = (3.0 + 1e-3 * rng.standard_normal(2 * c.n_probes)).astype(np.float32)
+    run = HipRun(c, theta, tokens)
+    assert run.update(7, losses) == 0
+    got = run.theta()
+    elems = []
+    for tid, off, rows, cols in oracle.layout(ocfg(c)):
+        n = rows * cols
+        elems.append(off + rng.choice(n, size=min(n, 30000), replace=False))
+        elems.append(np.array([off, off + cols - 1, off + n - cols, off + n - 1]))
+    elems = np.unique(np.concatenate(elems)).astype(np.int64)
+    ref = theta.copy()
+    assert oracle.update(ocfg(c), ref, 7, losses, elems=elems) == 0
+    a, r = as_f64(got[elems]), as_f64(ref[elems])
+    assert np.mean(got[elems] != ref[elems]) < 1e-3
+    assert np.abs(a - r).max() <= 2e-2 * np.abs(r).max()
+    assert np.mean(a != as_f64(theta[elems])) > 0.01
+    run.close()
 
 
 def test_nonfinite_loss_leaves_theta(oracle):

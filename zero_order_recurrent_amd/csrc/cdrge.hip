@@ -208,6 +208,8 @@ struct cdrge_ctx {
   char* ws = nullptr;
   hipStream_t stream = nullptr;
   int device = 0;
+  int n_cu = 1;  // compute units of the device
+  bool update_perm = false;  // the update runs k_update_perm
   bool timing = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[4];
   std::vector<hipEvent_t> event_pool;
@@ -481,6 +483,17 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
   return CDRGE_OK;
 }
 
+// The permute-addressed update takes bf16 parameters, K <= 64, all tensors in one launch and
+// 32-bit segment indices within a tensor.
+bool update_perm_ok(const Plan& p) {
+  if (p.cfg.dtype != CDRGE_BF16 || p.K > kUpdPermMaxProbes ||
+      static_cast<int>(p.tensors.size()) > kUpdMaxTensors)
+    return false;
+  for (const TensorDesc& t : p.tensors)
+    if (t.rows * ((t.cols + 127) / 128) >= (int64_t{1} << 31)) return false;
+  return true;
+}
+
 cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) {
   const Plan& p = ctx->plan;
   const hipStream_t s = ctx->stream;
@@ -506,12 +519,22 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
       ut.rows[i] = static_cast<int>(t.rows);
       ut.cols[i] = static_cast<int>(t.cols);
     }
+    const double bytes = 2.0 * double(p.d) * esz;
+    void* th = ctx->params;
+    if (ctx->update_perm) {
+      // one resident workgroup of 1,024 threads per compute unit, striding over the segments
+      const int64_t need = (segs + kUpdPermThreads / 4 - 1) / (kUpdPermThreads / 4);
+      const dim3 pgrid(static_cast<uint32_t>(need < ctx->n_cu ? need : ctx->n_cu));
+      const size_t lds = update_perm_bytes(p.K);
+      return timed(ctx, 2, bytes, [&] {
+        hipLaunchKernelGGL(k_update_perm, pgrid, dim3(kUpdPermThreads), lds, s,
+                           static_cast<uint16_t*>(th), ut, seeds, losses, p.K, coef, flags);
+      });
+    }
     const int64_t blocks = (segs + kUpdLutThreads / 4 - 1) / (kUpdLutThreads / 4);
     const dim3 lgrid(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096));
-    const double bytes = 2.0 * double(p.d) * esz;
     const int copies = update_lut_copies(p.K);
     const size_t lds = update_lut_bytes(p.K);
-    void* th = ctx->params;
     return timed(ctx, 2, bytes, [&] {
       if (bf16) {
         uint16_t* t = static_cast<uint16_t*>(th);
@@ -549,8 +572,23 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
   return CDRGE_OK;
 }
 
-// Allows the update kernel for K probes its table LDS.
-hipError_t set_update_lds(int K, bool bf16) {
+// Picks the update kernel and allows it its table LDS. The permute-addressed kernel addresses
+// its tables from LDS address 0, which holds while the kernel has no static LDS (checked here).
+hipError_t set_update_lds(cdrge_ctx* ctx, bool bf16) {
+  const Plan& p = ctx->plan;
+  const int K = p.K;
+  ctx->update_perm = false;
+  if (update_perm_ok(p)) {
+    const void* f = reinterpret_cast<const void*>(k_update_perm);
+    hipFuncAttributes fa{};
+    const hipError_t e = hipFuncGetAttributes(&fa, f);
+    if (e != hipSuccess) return e;
+    if (fa.sharedSizeBytes == 0) {
+      ctx->update_perm = true;
+      return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(update_perm_bytes(K)));
+    }
+  }
   const int copies = update_lut_copies(K);
   const int bytes = static_cast<int>(update_lut_bytes(K));
   const void* f = nullptr;
@@ -567,17 +605,19 @@ hipError_t set_update_lds(int K, bool bf16) {
 
 cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   CDRGE_HIP(hipGetDevice(&ctx->device));
+  CDRGE_HIP(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, ctx->device));
+  if (ctx->n_cu < 1) ctx->n_cu = 1;
   if (cfg->dtype == CDRGE_BF16) {
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_gates_bf16),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
-    CDRGE_HIP(set_update_lds(ctx->plan.K, true));
+    CDRGE_HIP(set_update_lds(ctx, true));
   } else {
     const Plan& p = ctx->plan;
     const int lds = static_cast<int>(
         sizeof(float) * f32_lds_layout(p.L, p.V, p.E, p.H, p.f32_g, p.f32_nb, p.f32_threads).total);
     CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(f32_kernel(p.f32_g, p.f32_nb)),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    CDRGE_HIP(set_update_lds(ctx->plan.K, false));
+    CDRGE_HIP(set_update_lds(ctx, false));
   }
   uint32_t* flags = ctx->at<uint32_t>(ctx->plan.off_flags);
   hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, ctx->stream, flags, 0u);

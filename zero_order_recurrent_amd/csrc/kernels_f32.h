@@ -93,7 +93,7 @@ __host__ __device__ inline F32Lds f32_lds_layout(int L, int V, int E, int H, int
   o.z = at;    at += f32_pad4(V * M);                     // [V][M]
   o.loss = at; at += f32_pad4(M);                         // [M]
   // signed partial sums of the layer input and of h: [word][nibble][slot][16]
-  const int wx = (E > H ? E : H) + 31 >> 5, wh = (H + 31) >> 5;
+  const int wx = ((E > H ? E : H) + 31) >> 5, wh = (H + 31) >> 5;
   o.tab = at;  at += wx * 8 * M * 16;
   o.tab_h = at; at += wh * 8 * M * 16;
   o.total = at;

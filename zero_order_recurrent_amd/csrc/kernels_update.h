@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels_common.h"
 
 namespace cdrge {
@@ -256,6 +258,306 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
     cur = next;
 #pragma unroll
     for (int v = 0; v < kVec; ++v) wv[v] = wn[v];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same update for bf16 parameters and K <= kUpdPermMaxProbes, with look-up addresses built by
+// one byte permute.
+//
+// Table copy o = g C + c (probe group g, copy c of C) keeps its 256 entries 256 bytes apart:
+// entry m at byte 65536 (o >> 6) + 256 m + 4 (o & 63). The byte address of a look-up is then the
+// byte string [4 (o & 63), m, o >> 6, 0], which v_perm_b32 assembles from index byte m of a
+// transposed sign word and a per-lane constant (no shift, no add). Lane l reads copy l % C; the
+// copies are C consecutive banks, so only lanes a multiple of C apart can meet in a bank.
+// Lanes form 4 rows of 16: the 16 lanes of a row take 16 consecutive 128-column segments, and
+// row w computes block w (columns 32w .. 32w + 31) of each. The four lanes of a segment are 16
+// apart, so a 4 x 4 exchange among them is two row swaps (v_permlane16_swap, v_permlane32_swap)
+// per four registers. It serves the sign words, and the parameters: memory is accessed with lane
+// (w, s) moving 16-byte piece w of each block of segment s (64 contiguous bytes per segment and
+// instruction), and the exchange turns that into, or back from, the four pieces of block w.
+// The Philox keys of every probe and round are precomputed in LDS (k0 + r 0x9E3779B9,
+// k1 + r 0xBB67AE85), and each segment's parameters are requested one segment ahead, alternating
+// between two register buffers.
+constexpr int kUpdPermThreads = 1024;
+constexpr int kUpdPermMaxProbes = 64;
+// Copies per group: the largest power of two up to 32 with G C <= 128 (at most two 64 KB regions).
+__host__ __device__ inline int update_perm_copies(int K) {
+  const int G = (K + 7) / 8;
+  int c = 32;
+  while (c > 1 && G * c > 128) c >>= 1;
+  return c;
+}
+__host__ __device__ inline int update_perm_regions(int K) {
+  return ((K + 7) / 8 * update_perm_copies(K) + 63) / 64;
+}
+// Dynamic LDS: the tables, then the key schedules [8 G][10], the loss differences [8 G], a flag,
+// and the tensor table (segment ends, offsets, column counts) that locates a segment without
+// vector memory loads (whose wait would also wait for the previous segment's stores).
+inline size_t update_perm_bytes(int K) {
+  const size_t kp = 8 * static_cast<size_t>((K + 7) / 8);
+  return 65536 * static_cast<size_t>(update_perm_regions(K)) + 80 * kp + 4 * kp + 16 +
+         kUpdMaxTensors * (8 + 8 + 4);
+}
+
+__device__ __forceinline__ PhiloxOut philox10_ks(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 const uint2* ks) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint2 k = ks[r];
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k.x);
+    const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k.y);
+    c0 = n0;
+    c1 = static_cast<uint32_t>(p1);
+    c2 = n2;
+    c3 = static_cast<uint32_t>(p0);
+  }
+  return PhiloxOut{c0, c1, c2, c3};
+}
+
+// 4 x 4 exchange among the lanes 16, 32 and 48 apart: afterwards a, b, c, d in row w hold what
+// rows 0, 1, 2, 3 held in register w (a for w = 0, ..., d for w = 3).
+__device__ __forceinline__ void row_exchange(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
+  const auto s01 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(c, d, false, false);
+  const auto t02 = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+  const auto t13 = __builtin_amdgcn_permlane32_swap(s01[1], s23[1], false, false);
+  a = t02[0];
+  b = t13[0];
+  c = t02[1];
+  d = t13[1];
+}
+__device__ __forceinline__ void row_exchange(uint4 (&p)[4]) {
+  row_exchange(p[0].x, p[1].x, p[2].x, p[3].x);
+  row_exchange(p[0].y, p[1].y, p[2].y, p[3].y);
+  row_exchange(p[0].z, p[1].z, p[2].z, p[3].z);
+  row_exchange(p[0].w, p[1].w, p[2].w, p[3].w);
+}
+
+// Keeps a parameter buffer in its registers up to this point (an empty asm that reads them). Put
+// between a buffer's stores and its reload, it keeps the address arithmetic of the reload out of
+// those registers: an ALU write there would first wait for the stores to complete, while the
+// reload itself, a memory load, is ordered after them.
+__device__ __forceinline__ void hold_buffer(const uint4 (&w)[4]) {
+  asm volatile("" ::"v"(w[0].x), "v"(w[0].y), "v"(w[0].z), "v"(w[0].w), "v"(w[1].x), "v"(w[1].y),
+               "v"(w[1].z), "v"(w[1].w), "v"(w[2].x), "v"(w[2].y), "v"(w[2].z), "v"(w[2].w),
+               "v"(w[3].x), "v"(w[3].y), "v"(w[3].z), "v"(w[3].w));
+}
+
+// A float in LDS addressed by its byte address (the kernel has no static LDS, so its dynamic
+// LDS, and with it the tables, starts at address 0).
+typedef __attribute__((address_space(3))) const float LdsFloat;
+
+__global__ __launch_bounds__(kUpdPermThreads) void k_update_perm(
+    uint16_t* __restrict__ theta_all, UpdTensors tens, const uint64_t* __restrict__ seeds,
+    const float* __restrict__ losses, int K, float coef, uint32_t* __restrict__ flags) {
+  extern __shared__ __align__(16) uint64_t upd_smem[];
+  char* const lds = reinterpret_cast<char*>(upd_smem);
+  const int G = (K + 7) / 8, C = update_perm_copies(K), R = update_perm_regions(K);
+  uint2* skeys = reinterpret_cast<uint2*>(lds + 65536 * R);
+  float* sdif = reinterpret_cast<float*>(skeys + 80 * G);
+  int* bad = reinterpret_cast<int*>(sdif + 8 * G);
+  int64_t* t_end = reinterpret_cast<int64_t*>(sdif + 8 * G + 4);
+  int64_t* t_off = t_end + kUpdMaxTensors;
+  int* t_cols = reinterpret_cast<int*>(t_off + kUpdMaxTensors);
+  const int tid = threadIdx.x;
+  if (tid == 0) *bad = 0;
+  if (tid < tens.n) {
+    t_end[tid] = tens.seg_end[tid];
+    t_off[tid] = tens.off[tid];
+    t_cols[tid] = tens.cols[tid];
+  }
+  __syncthreads();
+  for (int i = tid; i < 8 * G; i += kUpdPermThreads) {
+    float dv = 0.f;
+    if (i < K) {
+      const float lp = losses[2 * i], lm = losses[2 * i + 1];
+      if (!isfinite(lp) || !isfinite(lm)) atomicOr(bad, 1);
+      dv = lp - lm;
+    }
+    sdif[i] = dv;  // probes past K contribute nothing
+  }
+  for (int i = tid; i < 80 * G; i += kUpdPermThreads) {
+    const int pr = i / 10, r = i - 10 * pr;
+    const uint64_t sd = pr < K ? seeds[pr] : 0;
+    skeys[i] = make_uint2(static_cast<uint32_t>(sd) + static_cast<uint32_t>(r) * 0x9E3779B9u,
+                          static_cast<uint32_t>(sd >> 32) + static_cast<uint32_t>(r) * 0xBB67AE85u);
+  }
+  __syncthreads();
+  if (*bad) {
+    if (tid == 0 && blockIdx.x == 0) flags[0] = 1u;
+    return;
+  }
+  // float e of the table area is entry m = (e >> 6) & 255 of copy o = 64 (e >> 14) + (e & 63)
+  float* lut = reinterpret_cast<float*>(lds);
+  for (int e = tid; e < 16384 * R; e += kUpdPermThreads) {
+    const int o = 64 * (e >> 14) + (e & 63), m = (e >> 6) & 255;
+    if (o >= G * C) continue;
+    const int g = o / C;
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float dv = sdif[8 * g + k];
+      t += ((m >> k) & 1) ? -dv : dv;  // sign bit set: p = -1
+    }
+    lut[e] = t;
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, row = lane >> 4, wave = tid >> 6;
+  const int cpy = lane & (C - 1);
+  const int64_t nseg = tens.seg_end[tens.n - 1];
+  struct Seg {
+    uint16_t* tb;    // first parameter of the segment
+    int r, blk;
+    uint32_t id;
+    uint32_t fmask;  // bit j < 4: block j is a whole, 16-byte aligned 32-column block; bit 4: valid
+  };
+  // segments past the end are located as the last one and flagged invalid (no load or store)
+  auto locate = [&](int64_t seg) {
+    Seg g;
+    const bool valid = seg < nseg;
+    const int64_t sg = valid ? seg : nseg - 1;
+    int ti = 0;
+    while (sg >= t_end[ti]) ++ti;
+    const uint32_t local = static_cast<uint32_t>(sg - (ti ? t_end[ti - 1] : 0));
+    const int cols = t_cols[ti];
+    const uint32_t spr = static_cast<uint32_t>((cols + 127) / 128);
+    const uint32_t r = local / spr;
+    g.r = static_cast<int>(r);
+    g.blk = static_cast<int>(local - r * spr);
+    g.id = static_cast<uint32_t>(ti);
+    g.tb = theta_all + t_off[ti] + static_cast<int64_t>(g.r) * cols + 128 * g.blk;
+    const int rem = cols - 128 * g.blk;
+    const bool aligned = (reinterpret_cast<uintptr_t>(g.tb) & 15u) == 0;
+    g.fmask = valid ? (16u | (aligned ? (rem >= 128 ? 15u : (1u << (rem >> 5)) - 1u) : 0u)) : 0u;
+    return g;
+  };
+  // Piece `row` of every block of the segment. Issued for every lane and every segment, so that
+  // the number of loads in flight never depends on the path taken and the wait for a buffer never
+  // waits for the loads into the other one; pieces of blocks that are not whole read the first
+  // parameters instead (a model has at least 32) and are not used.
+  auto load_pieces = [&](const Seg& g, uint4 (&wv)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t* src = ((g.fmask >> j) & 1u) ? g.tb + 32 * j + 8 * row : theta_all;
+      wv[j] = *reinterpret_cast<const uint4*>(src);
+    }
+  };
+  auto process = [&](const Seg& cur, uint4 (&wv)[4]) {
+    float acc[32];
+    // first_tag: std::true_type for group 0, whose look-ups initialise the sums
+    auto group = [&](int g, auto first_tag) {
+      constexpr bool kFirst = decltype(first_tag)::value;
+      // row w evaluates probes 8g + 2w and 8g + 2w + 1 on this lane's segment
+      const uint2* ks = skeys + (8 * g + 2 * row) * 10;
+      const uint32_t blk = static_cast<uint32_t>(cur.blk), rr = static_cast<uint32_t>(cur.r);
+      const PhiloxOut o0 = philox10_ks(blk, rr, cur.id, 0u, ks);
+      const PhiloxOut o1 = philox10_ks(blk, rr, cur.id, 0u, ks + 10);
+      uint32_t v0[4] = {o0.x, o0.y, o0.z, o0.w}, v1[4] = {o1.x, o1.y, o1.z, o1.w};
+      // afterwards v[w] is word `row` (this lane's 32 columns) of the block of row w's probe
+      row_exchange(v0[0], v0[1], v0[2], v0[3]);
+      row_exchange(v1[0], v1[1], v1[2], v1[3]);
+      // X[j]: word `row` of probe 8g + j
+      uint32_t X[8] = {v0[0], v1[0], v0[1], v1[1], v0[2], v1[2], v0[3], v1[3]};
+      // 8x8 bit transposes inside each byte: afterwards bit j of byte b of X[k] is bit 8b + k
+      // of the word of probe 8g + j
+      auto swap_bits = [](uint32_t& lo, uint32_t& hi, int sh, uint32_t msk) {
+        const uint32_t x = ((lo >> sh) ^ hi) & msk;
+        hi ^= x;
+        lo ^= x << sh;
+      };
+      swap_bits(X[0], X[4], 4, 0x0F0F0F0Fu);
+      swap_bits(X[1], X[5], 4, 0x0F0F0F0Fu);
+      swap_bits(X[2], X[6], 4, 0x0F0F0F0Fu);
+      swap_bits(X[3], X[7], 4, 0x0F0F0F0Fu);
+      swap_bits(X[0], X[2], 2, 0x33333333u);
+      swap_bits(X[1], X[3], 2, 0x33333333u);
+      swap_bits(X[4], X[6], 2, 0x33333333u);
+      swap_bits(X[5], X[7], 2, 0x33333333u);
+      swap_bits(X[0], X[1], 1, 0x55555555u);
+      swap_bits(X[2], X[3], 1, 0x55555555u);
+      swap_bits(X[4], X[5], 1, 0x55555555u);
+      swap_bits(X[6], X[7], 1, 0x55555555u);
+      const int o = g * C + cpy;
+      const uint32_t y = (static_cast<uint32_t>(o & 63) << 2) | (static_cast<uint32_t>(o >> 6) << 16);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          // address bytes: [y byte 0, byte b of X[k], y byte 2, 0]
+          const uint32_t addr = __builtin_amdgcn_perm(X[k], y, 0x0C020400u | ((4u + b) << 8));
+          const float v = *reinterpret_cast<const LdsFloat*>(static_cast<uintptr_t>(addr));
+          if constexpr (kFirst)
+            acc[8 * b + k] = v;
+          else
+            acc[8 * b + k] += v;
+        }
+    };
+    group(0, std::true_type{});
+    for (int g = 1; g < G; ++g) group(g, std::false_type{});
+
+    // wv[v] becomes piece v of this lane's block; the results go back the same way
+    row_exchange(wv);
+    // Bit position p of the word is column 2 (p & 15) + (p >> 4): pair k of the 32 columns (16
+    // 32-bit pairs) holds bit positions k (low half) and k + 16 (high half).
+    const uint32_t in[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
+                             wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
+    uint32_t out[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float lo = __uint_as_float(in[k] << 16) - coef * acc[k];
+      const float hi = __uint_as_float(in[k] & 0xffff0000u) - coef * acc[k + 16];
+      // packed round-to-nearest-even conversion (identical to f32_to_bf16_rne for non-NaN)
+      const f32x2 v = {lo, hi};
+      out[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
+    row_exchange(wv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((cur.fmask >> j) & 1u) *reinterpret_cast<uint4*>(cur.tb + 32 * j + 8 * row) = wv[j];
+    // a valid block that is not whole (a row's last columns, or unaligned): element by element
+    if ((cur.fmask & 16u) && !((cur.fmask >> row) & 1u)) {
+      const int c0 = 128 * cur.blk + 32 * row, cols = t_cols[cur.id];
+      uint16_t* t = cur.tb + 32 * row;
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int cl = 2 * (p & 15) + (p >> 4);
+        if (c0 + cl < cols)
+          t[cl] = static_cast<uint16_t>(f32_to_bf16_rne(bf16_to_f32(t[cl]) - coef * acc[p]));
+      }
+    }
+  };
+
+  // Every lane runs every iteration (the row swaps need all 64 lanes); the wave's first segment
+  // decides the trip count.
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * (kUpdPermThreads / 4);
+  int64_t base = static_cast<int64_t>(blockIdx.x) * (kUpdPermThreads / 4) + 16 * wave;
+  if (base >= nseg) return;
+  const int sl = lane & 15;
+  Seg sa = locate(base + sl), sb;
+  uint4 wa[4], wb[4];
+  load_pieces(sa, wa);
+  for (;;) {
+    // the next segment (past the end: an invalid one) is requested before this one is computed
+    base += stride;
+    const bool more = base < nseg;
+    sb = locate(base + sl);
+    hold_buffer(wb);
+    load_pieces(sb, wb);
+    process(sa, wa);
+    if (!more) break;
+    base += stride;
+    const bool more2 = base < nseg;
+    sa = locate(base + sl);
+    hold_buffer(wa);
+    load_pieces(sa, wa);
+    process(sb, wb);
+    if (!more2) break;
   }
 }
 
