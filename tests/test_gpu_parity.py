@@ -110,11 +110,12 @@ def test_signs_bit_exact_through_update(oracle, dtype):
             run.close()
 
 
-# bf16 with K <= 64 runs the permute-addressed update: K = 8, 24, 40 and 64 give 1, 3, 5 and 8
-# probe groups in 32, 32, 16 and 16 table copies (one or two 64 KB regions). Otherwise K = 24, 300
-# and 600 keep 4, 2 and 1 copies of the probe-group tables in LDS.
+# bf16 with K <= 64 runs the permute-addressed update: K = 8, 13, 24, 40, 57 and 64 give 1, 2, 3,
+# 5, 8 and 8 probe groups (13 and 57 with unused probe slots) in 32, 32, 32, 16, 16 and 16 table
+# copies (one or two 64 KB regions). Otherwise K = 24, 300 and 600 keep 4, 2 and 1 copies of the
+# probe-group tables in LDS.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n_probes", [8, 24, 40, 64, 300, 600])
+@pytest.mark.parametrize("n_probes", [8, 13, 24, 40, 57, 64, 300, 600])
 def test_update_parity_identical_losses(oracle, dtype, n_probes):
     c = b.make_config(2, 50, 64, 192, 3, 2, n_probes, dtype, 1e-3, 1e-3, 99)
     say(f"[gpu] update parity {dtype} K={n_probes}")
