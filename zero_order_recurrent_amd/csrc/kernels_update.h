@@ -8,10 +8,14 @@
 // are taken 8 at a time: a table T_g[m] = sum_k (bit k of m ? -d_{8g+k} : d_{8g+k}) of all 256
 // signed partial sums is built once per workgroup in LDS, and each element adds T_g at the 8-bit
 // index formed by its 8 sign bits. The sign words arrive probe-major (one Philox block per probe
-// and 128-column segment), so each quad of lanes (one lane per 32-column word of a segment)
-// evaluates 8 probes' blocks, exchanges words with two DPP butterflies so that every lane holds
-// its own word of all 8 probes, and transposes those 8 words bitwise (three swap stages) so that
-// byte b of word k is the index of bit position 8b + k.
+// and 128-column segment), so the four lanes of a segment (one per 32-column word) evaluate 8
+// probes' blocks, exchange words so that every lane holds its own word of all 8 probes, and
+// transpose those 8 words bitwise (three swap stages) so that byte b of word k is the index of
+// bit position 8b + k.
+//
+// Two kernels: k_update_perm (bf16, K <= 64: lanes of a segment 16 apart, permute-addressed
+// tables, below) and k_update_lut (any dtype, K <= 1,024: a quad of adjacent lanes per segment,
+// DPP exchanges, tables in 4, 2 or 1 copies).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
