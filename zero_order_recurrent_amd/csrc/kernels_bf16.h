@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels_common.h"
 #include "kernels_gates_bf16.h"
 
@@ -26,8 +28,11 @@ __device__ __forceinline__ uint32_t pair_mask(uint32_t word, int m) {
 // ---------------------------------------------------------------------------------------------
 // Perturbed logits + cross-entropy of the last layer at timestep t, for every probe pair.
 // Tile: 64 logit rows (V <= 64, padded) x (128 columns of the +eps model, 128 of the -eps model).
-// waves: (64-column half, model); each wave owns 64 x 64 = 4 x 4 MFMA tiles. The softmax over the
-// 64 rows of one column spans the 4 lane groups of a wave, reduced with cross-lane shuffles.
+// waves: (64-column half, model); each wave owns 64 x 64 = 4 x 4 MFMA tiles. The perturbed W_out
+// tiles go through LDS (double-buffered); h goes from global memory straight into each wave's MFMA
+// B registers (the k-chunk-major layout makes a lane's 8 values of a fragment 16 contiguous bytes),
+// two chunks ahead. The softmax over the 64 rows of one column spans the 4 lane groups of a wave,
+// reduced with cross-lane shuffles.
 // seq[m][b] accumulates sum_t (logsumexp - logit of the next token) in float, in t order.
 //
 // kSplit: when the grid (column blocks x pairs) is too small to fill the chip, the reduction over
@@ -36,9 +41,10 @@ __device__ __forceinline__ uint32_t pair_mask(uint32_t word, int m) {
 // cross-entropy.
 // ---------------------------------------------------------------------------------------------
 constexpr int kCeRows = 64;
-constexpr int kCeTargetWorkgroups = 512;  // split the reduction below this many workgroups
-constexpr size_t kCeLdsBytes =
-    sizeof(uint16_t) * (2 * 2 * kCeRows * kCeLdsStride + 2 * 2 * kCeCols * kCeLdsStride);
+// Split the reduction below this many workgroups (one per CU). Measured on MI355X: splitting
+// charlm's 512 workgroups, or targeting 512 or 768, was slower than leaving 256+ unsplit.
+constexpr int kCeTargetWorkgroups = 256;
+constexpr size_t kCeLdsBytes = sizeof(uint16_t) * 2 * 2 * kCeRows * kCeLdsStride;
 
 struct CeArgs {
   const uint16_t* wp;
@@ -59,7 +65,6 @@ template <bool kSplit>
 __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* As = smem;                                  // [buf][side][64][40]
-  uint16_t* Bs = smem + 2 * 2 * kCeRows * kCeLdsStride;   // [buf][256][40]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ch = wave & 1, side = wave >> 1;
   const int H = a.H;
@@ -70,23 +75,19 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   const bool former = tid < kCeRows;
   const bool frow_ok = tid < a.V;
   const int frow = frow_ok ? tid : 0;
-  const int bq = tid & 3;
-  int64_t bcol_g[4];
-  bool bvalid[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = (tid >> 2) + 64 * j;
-    const int b = bcol0 + (n & 127);
-    bvalid[j] = b < a.B;
-    bcol_g[j] = static_cast<int64_t>(2 * pr + (n >> 7)) * a.B + (bvalid[j] ? b : 0);
-  }
+  // h column of this lane in fragment j: model 2 pr + side, sequence bcol0 + 64 ch + 16 j + lane % 16.
+  // Columns past the batch read the next model's columns or the padding (at least 256 columns
+  // past the last model; their logits are not used).
+  const uint32_t hcol0 = static_cast<uint32_t>((2 * pr + side) * a.B + bcol0 + 64 * ch + (lane & 15));
+  const uint16_t* hlane = a.h + static_cast<int64_t>(hcol0) * kKChunk + 8 * (lane >> 4);
+  const int64_t hchunk = static_cast<int64_t>(a.ncols_pad) * kKChunk;
   const int nch = H / kKChunk;
   const int c_begin = kSplit ? blockIdx.z * a.kper : 0;
   const int c_end = kSplit ? min(nch, c_begin + a.kper) : nch;
-  uint4 rp[4], rm[4], rb[4];
+  uint4 rp[4], rm[4];
   PhiloxOut words{0, 0, 0, 0};
 
-  auto load = [&](int c) {
+  auto load_w = [&](int c) {
     if (former) {
       const uint16_t* wp = a.wp + static_cast<int64_t>(frow) * H + kKChunk * c;
       const uint16_t* wm = a.wm + static_cast<int64_t>(frow) * H + kKChunk * c;
@@ -96,11 +97,12 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
         rm[k] = frow_ok ? reinterpret_cast<const uint4*>(wm)[k] : make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  // h fragments of chunk c (clamped to the last chunk of the range)
+  auto load_h = [&](int c, bf16x8 (&b)[4]) {
+    const uint16_t* src = hlane + hchunk * min(c, c_end - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint16_t* src = a.h + (static_cast<int64_t>(c) * a.ncols_pad + bcol_g[j]) * kKChunk + 8 * bq;
-      rb[j] = bvalid[j] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(src + 16 * kKChunk * j);
   };
   auto form_store = [&](int c, int buf) {
     if (former) {
@@ -126,11 +128,6 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
         am[k] = make_uint4(minus[4 * k], minus[4 * k + 1], minus[4 * k + 2], minus[4 * k + 3]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = (tid >> 2) + 64 * j;
-      *reinterpret_cast<uint4*>(Bs + (buf * 2 * kCeCols + n) * kCeLdsStride + 8 * bq) = rb[j];
-    }
   };
 
   f32x4 acc[4][4];
@@ -138,13 +135,8 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](int buf) {
+  auto mma = [&](int buf, const bf16x8 (&bfr)[4]) {
     const uint16_t* A = As + ((buf * 2 + side) * kCeRows + (lane & 15)) * kCeLdsStride + 8 * (lane >> 4);
-    const uint16_t* Bp =
-        Bs + (buf * 2 * kCeCols + 128 * side + 64 * ch + (lane & 15)) * kCeLdsStride + 8 * (lane >> 4);
-    bf16x8 bfr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(Bp + 16 * j * kCeLdsStride);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x8 afr = *reinterpret_cast<const bf16x8*>(A + 16 * i * kCeLdsStride);
@@ -154,16 +146,28 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
     }
   };
 
-  load(c_begin);
+  // h of chunk c is in hb[(c - c_begin) % 2]; the request for chunk c + 2 goes out after chunk c
+  // is multiplied (requests past the range repeat its last chunk and are not used).
+  bf16x8 hb[2][4];
+  load_w(c_begin);
+  load_h(c_begin, hb[0]);
+  load_h(c_begin + 1, hb[1]);
   form_store(c_begin, 0);
   __syncthreads();
-  for (int c = c_begin; c < c_end; ++c) {
-    const int buf = (c - c_begin) & 1;
-    if (c + 1 < c_end) load(c + 1);
-    mma(buf);
-    if (c + 1 < c_end) form_store(c + 1, buf ^ 1);
+  auto ce_step = [&](int c, auto par_tag) {
+    constexpr int par = decltype(par_tag)::value;
+    if (c + 1 < c_end) load_w(c + 1);
+    mma(par, hb[par]);
+    load_h(c + 2, hb[par]);
+    if (c + 1 < c_end) form_store(c + 1, par ^ 1);
     __syncthreads();
+  };
+  int c = c_begin;
+  for (; c + 2 <= c_end; c += 2) {
+    ce_step(c, std::integral_constant<int, 0>{});
+    ce_step(c + 1, std::integral_constant<int, 1>{});
   }
+  if (c < c_end) ce_step(c, std::integral_constant<int, 0>{});
 
   const int m = 2 * pr + side;
   const int g = lane >> 4;
