@@ -82,8 +82,17 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
   float* sdif = reinterpret_cast<float*>(upd_smem + 8 * G);  // [8 G]
   float* lut = sdif + 8 * G;  // [group][copy][kUpdLutStride], 256 entries used
   __shared__ int bad;
+  // the tensor table, so that locating a segment issues no vector load (whose wait would also
+  // wait for the previous segment's stores)
+  __shared__ int64_t t_end[kUpdMaxTensors], t_off[kUpdMaxTensors];
+  __shared__ int t_cols[kUpdMaxTensors];
   const int tid = threadIdx.x;
   if (tid == 0) bad = 0;
+  if (tid < tens.n) {
+    t_end[tid] = tens.seg_end[tid];
+    t_off[tid] = tens.off[tid];
+    t_cols[tid] = tens.cols[tid];
+  }
   __syncthreads();
   for (int i = tid; i < 8 * G; i += kUpdLutThreads) {
     float dv = 0.f;
@@ -140,11 +149,14 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
     uint32_t id;
     int full;
   };
+  // Segments past the end are located as the last one and never written (full = 0).
   auto locate = [&](int64_t seg) {
+    const bool valid = seg < nseg;
+    const int64_t sg = valid ? seg : nseg - 1;
     int ti = 0;
-    while (seg >= tens.seg_end[ti]) ++ti;
-    const int64_t local = seg - (ti ? tens.seg_end[ti - 1] : 0);
-    const int cols = tens.cols[ti];
+    while (sg >= t_end[ti]) ++ti;
+    const int64_t local = sg - (ti ? t_end[ti - 1] : 0);
+    const int cols = t_cols[ti];
     const int segs_per_row = (cols + 127) / 128;
     Seg g;
     g.r = static_cast<int>(local / segs_per_row);
@@ -152,31 +164,30 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
     g.c0 = g.blk * 128 + 32 * ell;
     g.cols = cols;
     g.id = static_cast<uint32_t>(ti);
-    g.t = theta_all + tens.off[ti] + static_cast<int64_t>(g.r) * cols + g.c0;
-    g.full = (g.c0 + 32 <= cols) && ((reinterpret_cast<uintptr_t>(g.t) & 15u) == 0);
+    g.t = theta_all + t_off[ti] + static_cast<int64_t>(g.r) * cols + g.c0;
+    g.full = valid && (g.c0 + 32 <= cols) && ((reinterpret_cast<uintptr_t>(g.t) & 15u) == 0);
     return g;
   };
-  auto load32 = [](const Seg& g, uint4 (&wv)[kVec]) {
-    if (g.full) {
+  // Issued for every lane, so that the number of loads in flight does not depend on the path
+  // taken; lanes without a whole 32-column piece read the first parameters instead (a model has
+  // at least 32) and do not use them.
+  auto load32 = [&](const Seg& g, uint4 (&wv)[kVec]) {
+    const uint4* src = reinterpret_cast<const uint4*>(g.full ? g.t : theta_all);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) wv[v] = reinterpret_cast<const uint4*>(g.t)[v];
-    }
+    for (int v = 0; v < kVec; ++v) wv[v] = src[v];
   };
 
   int64_t seg = static_cast<int64_t>(blockIdx.x) * (kUpdLutThreads / 4) + (tid >> 2);
   if (seg >= nseg) return;
   Seg cur = locate(seg);
-  uint4 wv[kVec] = {};
+  uint4 wv[kVec];
   load32(cur, wv);
   for (; seg < nseg; seg += quads) {
-    // request the next segment's parameters first
+    // request the next segment's parameters first (past the end: an unused, clamped one)
     const int64_t nxt = seg + quads;
-    Seg next = cur;
-    uint4 wn[kVec] = {};
-    if (nxt < nseg) {
-      next = locate(nxt);
-      load32(next, wn);
-    }
+    const Seg next = locate(nxt);
+    uint4 wn[kVec];
+    load32(next, wn);
     float acc[32];
 #pragma unroll
     for (int p = 0; p < 32; ++p) acc[p] = 0.f;
