@@ -87,13 +87,15 @@ typedef struct {
 int64_t cdrge_param_count(const cdrge_config* cfg);
 
 /* CDRGE_OK if the configuration is valid and supported; otherwise the reason.
- * Supported: F32 with n_layers <= 8 and E, H, V <= 65536 when the on-chip state of one
- * workgroup - h and c of every layer, the gate pre-activations, the layer input and its tables of
- * signed partial sums for up to 2 probe pairs x 8 sequences - fits in 128 KB (about
- * 4 * m * (2 L H + 5 max(E, H) + 4 H) bytes for m = 2 * pairs * sequences per workgroup, plus
- * 8 L H bytes of biases); BF16 when E % 32 == 0,
- * H % 32 == 0, V <= 64, and one probe chunk's activations stay within 32-bit element offsets:
- * (2 * probes_per_chunk * B + 256) * max(E, H) < 2^31 and 4 H max(E, H) < 2^31. */
+ * Supported: n_probes <= 1024, and
+ *   F32 with n_layers <= 8 and E, H, V <= 65536 when the on-chip state of one workgroup - h and c
+ *   of every layer, the gate pre-activations, the layer input and its tables of signed partial
+ *   sums for up to 2 probe pairs x 8 sequences - fits in 128 KB (about
+ *   4 * m * (2 L H + 5 max(E, H) + 4 H) bytes for m = 2 * pairs * sequences per workgroup, plus
+ *   8 L H bytes of biases);
+ *   BF16 when E % 32 == 0, H % 32 == 0, V <= 64, and one probe chunk's activations stay within
+ *   32-bit element offsets: (2 * probes_per_chunk * B + 256) * max(E, H) < 2^31 and
+ *   4 H max(E, H) < 2^31. */
 cdrge_status cdrge_check_config(const cdrge_config* cfg);
 
 /* Device workspace, in bytes, that cdrge_init needs for this configuration (256-byte aligned

@@ -159,6 +159,24 @@ def test_signs_bit_exact_through_update_many_probes(oracle, dtype, n_probes, pro
         run.close()
 
 
+def test_update_parity_many_tensors(oracle):
+    # 10 bf16 layers: 33 tensors, more than one launch's tensor table holds, so the update runs
+    # per tensor with per-probe sign-adds.
+    c = b.make_config(10, 20, 32, 32, 2, 2, 12, "bf16", 1e-3, 1e-3, 98)
+    say("[gpu] update parity, 33 tensors, bf16")
+    theta, tokens = _inputs(c, 12)
+    rng = np.random.default_rng(6)
+    losses = (3.0 + 1e-3 * rng.standard_normal(2 * c.n_probes)).astype(np.float32)
+    run = HipRun(c, theta, tokens)
+    assert run.update(2, losses) == 0
+    ref = theta.copy()
+    assert oracle.update(ocfg(c), ref, 2, losses) == 0
+    got = run.theta()
+    assert_theta_close(oracle, c, got, ref, 2e-2)
+    assert np.mean(got != ref) < 1e-3
+    run.close()
+
+
 def test_update_many_segments(oracle):
     # bf16, K = 16, d = 16.1M: each update workgroup strides over the 128-column segments several
     # times (both parameter buffers in turn, and a partial last pass); W_ih has 1,056 columns, so
