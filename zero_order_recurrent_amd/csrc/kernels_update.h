@@ -169,12 +169,12 @@ __global__ __launch_bounds__(kUpdLutThreads) void k_update_lut(
     return g;
   };
   // Issued for every lane, so that the number of loads in flight does not depend on the path
-  // taken; lanes without a whole 32-column piece read the first parameters instead (a model has
-  // at least 32) and do not use them.
+  // taken; lanes without a whole 32-column piece read the first 16 bytes of the parameters
+  // instead, for every piece (a model has at least 15 parameters), and do not use them.
   auto load32 = [&](const Seg& g, uint4 (&wv)[kVec]) {
     const uint4* src = reinterpret_cast<const uint4*>(g.full ? g.t : theta_all);
 #pragma unroll
-    for (int v = 0; v < kVec; ++v) wv[v] = src[v];
+    for (int v = 0; v < kVec; ++v) wv[v] = src[g.full ? v : 0];
   };
 
   int64_t seg = static_cast<int64_t>(blockIdx.x) * (kUpdLutThreads / 4) + (tid >> 2);
@@ -452,8 +452,8 @@ __global__ __launch_bounds__(kUpdPermThreads) void k_update_perm(
   };
   // Piece `row` of every block of the segment. Issued for every lane and every segment, so that
   // the number of loads in flight never depends on the path taken and the wait for a buffer never
-  // waits for the loads into the other one; pieces of blocks that are not whole read the first
-  // parameters instead (a model has at least 32) and are not used.
+  // waits for the loads into the other one; pieces of blocks that are not whole read the first 16
+  // bytes of the parameters instead (a bf16 model has at least 32) and are not used.
   auto load_pieces = [&](const Seg& g, uint4 (&wv)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
