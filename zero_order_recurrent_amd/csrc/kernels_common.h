@@ -11,6 +11,20 @@ namespace cdrge {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
+// 4 x 4 exchange among the lanes 16, 32 and 48 apart (the four 16-lane rows of a wave):
+// afterwards a, b, c, d in row w hold what rows 0, 1, 2, 3 held in register w (a for w = 0, ...,
+// d for w = 3). Two v_permlane16_swap and two v_permlane32_swap; all 64 lanes must be active.
+__device__ __forceinline__ void row_exchange(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
+  const auto s01 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(c, d, false, false);
+  const auto t02 = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+  const auto t13 = __builtin_amdgcn_permlane32_swap(s01[1], s23[1], false, false);
+  a = t02[0];
+  b = t13[0];
+  c = t02[1];
+  d = t13[1];
+}
+
 // Nearest bf16 to x, ties to even; NaN stays a quiet NaN. (The carry of the rounding increment
 // propagates into the exponent, so values past the largest bf16 become infinity.)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {

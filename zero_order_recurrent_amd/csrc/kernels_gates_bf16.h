@@ -31,7 +31,7 @@
 //   * the selected tiles of both models live in an 8-stage LDS ring; fragments are read two row
 //     groups ahead of the MFMAs that use them; a barrier follows the select in every fourth step.
 // The cell state stays in accumulator order (tile-private, 16 bytes per lane and row group), and
-// h leaves through an LDS transpose as whole 64-byte column segments.
+// h leaves as whole 64-byte column segments, regrouped in registers by lane exchanges.
 // The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 16 row
 // tiles x 2 column blocks (or 8 x 4), which keeps their shared weight and activation chunks in
 // that XCD's L2.
@@ -55,7 +55,6 @@ constexpr int kUnitsPerTile = 32;
 constexpr int kTileRows = 4 * kUnitsPerTile;   // 128 gate rows
 constexpr int kTileCols = 256;                 // batch columns per model
 constexpr int kKChunk = 32;
-constexpr int kHsStride = 40;                  // bf16 per row of the h transpose buffer
 constexpr int kAStageBytes = 2 * kTileRows * 64;   // both models' 128 x 32 bf16 tiles
 constexpr int kAStages = 8;
 constexpr int kBRing = 4;                          // activation register ring (chunks)
@@ -65,8 +64,6 @@ constexpr int kBRing = 4;                          // activation register ring (
 // group_cols.
 constexpr size_t kGateBiasOffset = size_t(kAStages) * kAStageBytes;
 constexpr size_t kGateLdsBytes = kGateBiasOffset + sizeof(float) * 2 * 4 * kUnitsPerTile;  // + gate biases
-static_assert(sizeof(uint16_t) * 2 * kTileCols * kHsStride <= kGateBiasOffset,
-              "the h transpose buffer reuses the weight ring");
 
 // LSTM cell from the four gate pre-activations: sigmoid(x) = 1 / (1 + e^-x),
 // tanh(x) = 2 / (1 + e^-2x) - 1, c' = sigmoid(f) c + sigmoid(i) tanh(g), h = sigmoid(o) tanh(c').
@@ -327,12 +324,14 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   float4 cst[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) cst[i] = a.first ? make_float4(0.f, 0.f, 0.f, 0.f) : cptr[64 * i];
-  // Requests past the last chunk may still be in flight; the weight ring is reused below.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // ---- fused LSTM cell; h leaves through LDS as whole 64-byte column segments ----------------
-  uint16_t* Hs = smem;  // [512 columns][40], reused after the K loop
+  // ---- fused LSTM cell; h leaves from registers as whole 64-byte column segments -------------
+  // Lane (row r = lane / 16, column lane % 16 of each 16-column block j) holds unit 4 i + r of row
+  // group i. The bf16 h of row groups 2k and 2k + 1 share a register (units 8k + r and 8k + 4 + r),
+  // the four registers of a column block are exchanged among the four rows (row_exchange), and a
+  // byte permute re-pairs them so that row r holds units 8r .. 8r + 7: one 16-byte store per lane
+  // and column block, 1 KB of contiguous h per store instruction, without LDS or a barrier.
+  uint32_t hd[4][4];  // [j][k]: bf16 h of units 8k + r (low half) and 8k + 4 + r (high half)
+  float hprev[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ul = 4 * i + (lane >> 4);
@@ -342,27 +341,32 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     float cn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int cl = 64 * cq + 16 * j + (lane & 15);
       float hv;
       lstm_cell(acc[i][j][0] + bi, acc[i][j][1] + bf, acc[i][j][2] + bg, acc[i][j][3] + bo, cprev[j], cn[j], hv);
-      // hardware round-to-nearest-even conversion (equal to f32_to_bf16_rne except for NaN payloads)
-      const f32x2 hp = {hv, hv};
-      Hs[(256 * side + cl) * kHsStride + ul] =
-          static_cast<uint16_t>(__builtin_bit_cast(uint32_t, __builtin_convertvector(hp, bf16x2)));
+      if (i & 1) {
+        // hardware round-to-nearest-even conversion (equal to f32_to_bf16_rne except for NaN payloads)
+        const f32x2 hp = {hprev[j], hv};
+        hd[j][i >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hp, bf16x2));
+      } else {
+        hprev[j] = hv;
+      }
     }
     cptr[64 * i] = make_float4(cn[0], cn[1], cn[2], cn[3]);
   }
-  __syncthreads();
-  {
-    const int cidx = tid;  // 0..511
-    const int sd = cidx >> 8;
-    const int b = bcol0 + (cidx & 255);
-    if (b < a.B) {
-      const int64_t gcol = static_cast<int64_t>(2 * pr + sd) * a.B + b;
-      const uint4* src = reinterpret_cast<const uint4*>(Hs + cidx * kHsStride);
-      uint4* dst = reinterpret_cast<uint4*>(a.h_out + (static_cast<int64_t>(rt) * a.ncols_pad + gcol) * kKChunk);
+  const int hrow = lane >> 4;
+  const int64_t hcol0 = static_cast<int64_t>(2 * pr + side) * a.B;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) dst[v] = src[v];
+  for (int j = 0; j < 4; ++j) {
+    // afterwards hd[j][x] holds units 8 hrow + x (low half) and 8 hrow + 4 + x (high half)
+    row_exchange(hd[j][0], hd[j][1], hd[j][2], hd[j][3]);
+    const uint4 out = make_uint4(__builtin_amdgcn_perm(hd[j][1], hd[j][0], 0x05040100u),
+                                 __builtin_amdgcn_perm(hd[j][3], hd[j][2], 0x05040100u),
+                                 __builtin_amdgcn_perm(hd[j][1], hd[j][0], 0x07060302u),
+                                 __builtin_amdgcn_perm(hd[j][3], hd[j][2], 0x07060302u));
+    const int b = bcol0 + 64 * cq + 16 * j + (lane & 15);
+    if (b < a.B) {
+      uint16_t* dst = a.h_out + (static_cast<int64_t>(rt) * a.ncols_pad + hcol0 + b) * kKChunk + 8 * hrow;
+      *reinterpret_cast<uint4*>(dst) = out;
     }
   }
 }

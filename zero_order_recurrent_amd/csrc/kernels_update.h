@@ -332,18 +332,7 @@ __device__ __forceinline__ PhiloxOut philox10_ks(uint32_t c0, uint32_t c1, uint3
   return PhiloxOut{c0, c1, c2, c3};
 }
 
-// 4 x 4 exchange among the lanes 16, 32 and 48 apart: afterwards a, b, c, d in row w hold what
-// rows 0, 1, 2, 3 held in register w (a for w = 0, ..., d for w = 3).
-__device__ __forceinline__ void row_exchange(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
-  const auto s01 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  const auto s23 = __builtin_amdgcn_permlane16_swap(c, d, false, false);
-  const auto t02 = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
-  const auto t13 = __builtin_amdgcn_permlane32_swap(s01[1], s23[1], false, false);
-  a = t02[0];
-  b = t13[0];
-  c = t02[1];
-  d = t13[1];
-}
+// row_exchange of four 16-byte registers, one 32-bit component at a time.
 __device__ __forceinline__ void row_exchange(uint4 (&p)[4]) {
   row_exchange(p[0].x, p[1].x, p[2].x, p[3].x);
   row_exchange(p[0].y, p[1].y, p[2].y, p[3].y);
