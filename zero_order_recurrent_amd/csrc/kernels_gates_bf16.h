@@ -47,6 +47,7 @@ namespace cdrge {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -321,9 +322,13 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // row group is one 16-byte access per lane and 1 KB per wave.
   const int64_t tile = (static_cast<int64_t>(pr) * a.n_col_blocks + cb) * a.n_row_tiles + rt;
   float4* cptr = reinterpret_cast<float4*>(a.c_tile) + (tile * 8 + wave) * 8 * 64 + lane;
-  float4 cst[8];
+  // The cell state is read and written once per launch by this workgroup alone: its accesses
+  // (and the h stores) are marked non-temporal, which keeps them from displacing the weight and
+  // activation lines that the workgroups of an XCD share in L2 (charlm launch -1.5 to -2.2%).
+  f32x4 cst[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cst[i] = a.first ? make_float4(0.f, 0.f, 0.f, 0.f) : cptr[64 * i];
+  for (int i = 0; i < 8; ++i)
+    cst[i] = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(cptr + 64 * i));
   // ---- fused LSTM cell; h leaves from registers as whole 64-byte column segments -------------
   // Lane (row r = lane / 16, column lane % 16 of each 16-column block j) holds unit 4 i + r of row
   // group i. The bf16 h of row groups 2k and 2k + 1 share a register (units 8k + r and 8k + 4 + r),
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     const int ul = 4 * i + (lane >> 4);
     const float* bs = bias_s + side * 4 * kUnitsPerTile + ul;
     const float bi = bs[0], bf = bs[kUnitsPerTile], bg = bs[2 * kUnitsPerTile], bo = bs[3 * kUnitsPerTile];
-    const float cprev[4] = {cst[i].x, cst[i].y, cst[i].z, cst[i].w};
+    const float cprev[4] = {cst[i][0], cst[i][1], cst[i][2], cst[i][3]};
     float cn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
         hprev[j] = hv;
       }
     }
-    cptr[64 * i] = make_float4(cn[0], cn[1], cn[2], cn[3]);
+    __builtin_nontemporal_store(f32x4{cn[0], cn[1], cn[2], cn[3]}, reinterpret_cast<f32x4*>(cptr + 64 * i));
   }
   const int hrow = lane >> 4;
   const int64_t hcol0 = static_cast<int64_t>(2 * pr + side) * a.B;
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     const int b = bcol0 + 64 * cq + 16 * j + (lane & 15);
     if (b < a.B) {
       uint16_t* dst = a.h_out + (static_cast<int64_t>(rt) * a.ncols_pad + hcol0 + b) * kKChunk + 8 * hrow;
-      *reinterpret_cast<uint4*>(dst) = out;
+      __builtin_nontemporal_store(u32x4{out.x, out.y, out.z, out.w}, reinterpret_cast<u32x4*>(dst));
     }
   }
 }
