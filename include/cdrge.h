@@ -145,7 +145,9 @@ const char* cdrge_last_error_detail(void);
 
 /* Diagnostics: when enabled, every launch is bracketed by HIP events on the context's stream
  * and its duration is added to a per-kind total. kind: 0 recurrent gate kernel, 1 logits and
- * cross-entropy, 2 update, 3 per-step preparation and loss reduction. */
+ * cross-entropy, 2 update, 3 per-step preparation and loss reduction. The events are timing-only
+ * (created without a system-scope fence), so recording them adds no cache write-back between
+ * kernels; they order nothing for other streams or the host. */
 cdrge_status cdrge_set_timing(cdrge_ctx* ctx, int enable);
 
 /* Total milliseconds and launch count per kind since the last reset (waits for the stream). */
