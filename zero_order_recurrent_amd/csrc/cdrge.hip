@@ -410,7 +410,8 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       const dim3 cgrid((p.B + kCeCols - 1) / kCeCols, pc);
       for (int t = 0; t < p.T; ++t) {
         {
-          const dim3 xgrid(static_cast<uint32_t>((4 * p.ncols_pad + 255) / 256), static_cast<uint32_t>(p.E / 32));
+          const dim3 xgrid(static_cast<uint32_t>((4 * p.ncols_pad + 255) / 256),
+                           static_cast<uint32_t>((p.E / 32 + kGatherChunks - 1) / kGatherChunks));
           CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
             hipLaunchKernelGGL(k_gather_x0, xgrid, dim3(256), 0, s, emb_m,
                                tokens, p.B, p.T, t, p.V, p.E, ncols, static_cast<int>(p.ncols_pad), x0);

@@ -150,21 +150,35 @@ __global__ void k_model_tensor_bf16(const uint16_t* __restrict__ src, int rows, 
 // holds emb_m[m][token(b, t)][:], the model's perturbed embedding row, stored k-chunk-major
 // like the h of a lower layer (element (column, e) at ((e / 32) ncols_pad + column) 32 + e % 32).
 // Columns ncols .. ncols_pad - 1 are zero. Tokens outside [0, V) are clamped (the step's losses
-// are NaN then anyway). One thread per 16-byte piece (E % 32 == 0); grid (ceil(4 ncols_pad / 256),
-// E / 32): blockIdx.y is the 32-wide chunk, and consecutive threads write consecutive pieces.
+// are NaN then anyway). E % 32 == 0. A thread owns one 16-byte piece of one column in each of
+// kGatherChunks consecutive 32-wide chunks (one token lookup for all of them, and their loads in
+// flight together); grid (ceil(4 ncols_pad / 256), ceil(E / 32 / kGatherChunks)), and consecutive
+// threads write consecutive pieces of a chunk.
+constexpr int kGatherChunks = 4;
 __global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* __restrict__ tokens, int B,
                             int T, int t, int V, int E, int ncols, int ncols_pad, uint16_t* __restrict__ x) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;  // 4 column + piece, < 4 ncols_pad
   if (i >= 4u * static_cast<uint32_t>(ncols_pad)) return;
-  const uint32_t col = i >> 2, p4 = i & 3, kc = blockIdx.y;
-  uint4 v = make_uint4(0, 0, 0, 0);
+  const uint32_t col = i >> 2, p4 = i & 3, kc0 = blockIdx.y * kGatherChunks;
+  const uint32_t nkc = static_cast<uint32_t>(E) / 32u;
+  uint4 v[kGatherChunks];
+  const uint4* row = nullptr;
   if (col < static_cast<uint32_t>(ncols)) {
     const uint32_t m = col / static_cast<uint32_t>(B), b = col - m * static_cast<uint32_t>(B);
     int tok = tokens[static_cast<int64_t>(b) * (T + 1) + t];
     tok = min(max(tok, 0), V - 1);
-    v = reinterpret_cast<const uint4*>(emb_m + (static_cast<int64_t>(m) * V + tok) * E)[4 * kc + p4];
+    row = reinterpret_cast<const uint4*>(emb_m + (static_cast<int64_t>(m) * V + tok) * E);
   }
-  reinterpret_cast<uint4*>(x)[static_cast<int64_t>(kc) * 4 * ncols_pad + i] = v;
+#pragma unroll
+  for (int j = 0; j < kGatherChunks; ++j) {
+    const uint32_t kc = kc0 + j;
+    v[j] = (row != nullptr && kc < nkc) ? row[4 * kc + p4] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kGatherChunks; ++j) {
+    const uint32_t kc = kc0 + j;
+    if (kc < nkc) reinterpret_cast<uint4*>(x)[static_cast<int64_t>(kc) * 4 * ncols_pad + i] = v[j];
+  }
 }
 
 // losses[m0 + m] = (sum_b seq[m][b]) / (B T) with a fixed-order double reduction (bitwise

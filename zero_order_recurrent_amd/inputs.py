@@ -53,7 +53,7 @@ PRESETS = {
     "charlm": Preset("charlm", 3, 2, 128, 1024, 50, "bf16", 1024, 10, 64, 1e-4, 1e-4, "zipf"),
     "lstm270m": Preset("lstm270m", 4, 2, 4096, 4096, 50, "bf16", 1024, 10, 32, 1e-4, 1e-4, "zipf"),
     "lstm1b": Preset("lstm1b", 5, 4, 5888, 5888, 50, "bf16", 256, 10, 16, 1e-4, 1e-4, "zipf",
-                     probes_per_chunk=4),
+                     probes_per_chunk=8),
 }
 
 
