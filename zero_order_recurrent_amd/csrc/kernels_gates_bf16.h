@@ -114,7 +114,8 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
   if (a.swizzle) {
     // Workgroups are dealt to the 8 XCDs round-robin; v enumerates one XCD's workgroups in
     // dispatch order, and each run of group_rows * group_cols of them covers group_rows row tiles
-    // x group_cols column blocks (the host checks the divisibility this needs).
+    // x group_cols column blocks. The host guarantees whole groups and a multiple of 8 workgroups
+    // (then v is a bijection); a run may start on one XCD and end on the next.
     const int n = gridDim.x;
     const int v = (L & 7) * (n >> 3) + (L >> 3);
     const int gr = a.group_rows, gsz = a.group_rows * a.group_cols;
