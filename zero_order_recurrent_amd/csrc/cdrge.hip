@@ -394,15 +394,17 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       const int n_rt = p.H / kUnitsPerTile;
       const int n_cb = (p.B + kTileCols - 1) / kTileCols;
       const int n_blocks = n_rt * n_cb * pc;
-      // The XCD-grouped order needs whole groups of group_rows row tiles x group_cols column
-      // blocks (16 x 2 where the row tiles allow it, else 8 x 4) and a multiple of 8 workgroups,
-      // so that the order is a bijection. An XCD's share need not be whole groups: a group may
-      // straddle two XCDs and share less in L2 (lstm1b: 1,472 tiles, 5.75 groups per XCD; its
-      // gate launch took 1.92 ms grouped against 2.03 ms in plain order).
+      // The XCD-grouped order takes groups of group_rows row tiles x group_cols column blocks
+      // (16 x 2, else 8 x 4), the last row group of each column group shorter when the row tiles
+      // do not divide by group_rows, and needs a multiple of 8 workgroups (then the order is a
+      // bijection). An XCD's share need not be whole groups: a group may straddle two XCDs and
+      // share less in L2. lstm1b (184 row tiles, 1,472 tiles) ran in plain order while whole
+      // groups per XCD were required: 2.03 ms per gate launch, 1.92 ms in 8 x 4 groups, 1.88 ms
+      // in 16 x 2 groups with a last group of 8 row tiles.
       int group_rows = 0, group_cols = 0;
       for (const int gr : {16, 8}) {
         const int gc = 32 / gr;
-        if (n_rt % gr == 0 && (n_cb * pc) % gc == 0 && n_blocks % (gr * gc) == 0 && n_blocks % 8 == 0) {
+        if (n_rt >= gr && (n_cb * pc) % gc == 0 && n_blocks % 8 == 0) {
           group_rows = gr;
           group_cols = gc;
           break;

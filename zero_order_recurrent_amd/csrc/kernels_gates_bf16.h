@@ -33,8 +33,8 @@
 // The cell state stays in accumulator order (tile-private, 16 bytes per lane and row group), and
 // h leaves as whole 64-byte column segments, regrouped in registers by lane exchanges.
 // The 1-D grid is ordered so that the 32 workgroups resident on one XCD at a time cover 16 row
-// tiles x 2 column blocks (or 8 x 4), which keeps their shared weight and activation chunks in
-// that XCD's L2.
+// tiles x 2 column blocks (or 8 x 4; the last row group of a column group may be shorter), which
+// keeps their shared weight and activation chunks in that XCD's L2.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -113,16 +113,26 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
   int rtile, cw;
   if (a.swizzle) {
     // Workgroups are dealt to the 8 XCDs round-robin; v enumerates one XCD's workgroups in
-    // dispatch order, and each run of group_rows * group_cols of them covers group_rows row tiles
-    // x group_cols column blocks. The host guarantees whole groups and a multiple of 8 workgroups
-    // (then v is a bijection); a run may start on one XCD and end on the next.
+    // dispatch order (a bijection when the grid is a multiple of 8, which the host guarantees).
+    // v runs through the column blocks group_cols at a time; within such a column group, each
+    // run of group_rows * group_cols workgroups covers group_rows row tiles x group_cols column
+    // blocks, and when the row tiles do not divide by group_rows the rest form one shorter group.
+    // A group may start on one XCD and end on the next.
     const int n = gridDim.x;
     const int v = (L & 7) * (n >> 3) + (L >> 3);
-    const int gr = a.group_rows, gsz = a.group_rows * a.group_cols;
-    const int g = v / gsz, q = v % gsz;
-    const int n_rg = a.n_row_tiles / gr;
-    rtile = (g % n_rg) * gr + q % gr;
-    cw = (g / n_rg) * a.group_cols + q / gr;
+    const int gr = a.group_rows, gc = a.group_cols, gsz = gr * gc;
+    const int per_cg = a.n_row_tiles * gc;
+    const int cg = v / per_cg, r = v - cg * per_cg;
+    const int n_full = a.n_row_tiles / gr;
+    if (r < n_full * gsz) {
+      const int g = r / gsz, q = r - g * gsz;
+      rtile = g * gr + q % gr;
+      cw = cg * gc + q / gr;
+    } else {
+      const int rem = a.n_row_tiles - n_full * gr, q = r - n_full * gsz;  // rem > 0 here
+      rtile = n_full * gr + q % rem;
+      cw = cg * gc + q / rem;
+    }
   } else {
     rtile = L % a.n_row_tiles;
     cw = L / a.n_row_tiles;
