@@ -198,17 +198,17 @@ int cdrge_update(const std::vector<TensorInfo>& lay, void* theta, Storage s, uin
   return 0;
 }
 
-// Mean LSTM loss over all B sequences (in double), rounded to float as the loss value.
+// Mean LSTM loss over the scored positions of all B sequences (in double).
 template <class P>
-double lstm_mean_loss(const ModelShape& m, const std::vector<P>& w, const int32_t* tokens,
+double lstm_mean_loss(const ModelShape& m, const std::vector<P>& w, const TokenView& tv,
                       bool round_act_bf16) {
   std::vector<int> ids(m.B);
   for (int b = 0; b < m.B; ++b) ids[b] = b;
   std::vector<double> seq(m.B);
-  lstm_sequence_losses<double, P>(m, w.data(), tokens, ids.data(), m.B, round_act_bf16, seq.data());
+  lstm_sequence_losses<double, P>(m, w.data(), tv, ids.data(), m.B, round_act_bf16, seq.data());
   double total = 0.0;
   for (int b = 0; b < m.B; ++b) total += seq[b];
-  return total / (static_cast<double>(m.B) * m.T);
+  return total / static_cast<double>(scored_positions(tv, m.T, ids.data(), m.B));
 }
 
 }  // namespace oracle

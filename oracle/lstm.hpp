@@ -14,6 +14,13 @@
 //   c_t = f * c_{t-1} + i * g,   h_t = o * tanh(c_t),   h_0 = c_0 = 0
 //   loss = (1 / (B T)) * sum_{b,t} [ logsumexp(z_{b,t}) - z_{b,t}[tok[b][t+1]] ]
 //
+// Inputs and targets. For language modelling the input at step t is tok[b][t] and the target is
+// the next token tok[b][t+1]. The synthetic transduction tasks the pages also train on (copy,
+// reverse, rolling sum; alex-wiki "Evidence And Limits") give inputs and targets separately, and
+// only the output part of a sequence is scored: a target below zero marks a position that adds
+// nothing to the loss, and the loss is the mean over the scored positions (torch's cross_entropy
+// with an ignore index and mean reduction). With every position scored this is the formula above.
+//
 // Flat parameter layout (tensor ids are what the Rademacher sign generator is keyed on):
 //   id 0: Emb [V][E];  for layer l: id 1+3l W_ih [4H][in_l] (in_0 = E, else H),
 //   id 2+3l W_hh [4H][H], id 3+3l b [1][4H];  id 1+3L W_out [V][H];  id 2+3L b_out [1][V].
@@ -101,12 +108,34 @@ inline S sigmoid(S x) {
 inline double act_round(double x, bool bf) { return bf ? round_to_bf16(x) : x; }
 inline Dual act_round(Dual x, bool bf) { return bf ? Dual(round_to_bf16(x.v), x.d) : x; }
 
-// Per-sequence loss sums sum_t l_{b,t} for the requested sequences.
+// Where the input and the target of (sequence b, step t) are read: inputs[b * in_stride + t] and
+// targets[b * tg_stride + t]; a target below zero is not scored.
+struct TokenView {
+  const int32_t* inputs;
+  int64_t in_stride;
+  const int32_t* targets;
+  int64_t tg_stride;
+};
+
+// The language-model view of tokens [B][T+1]: input tok[b][t], target tok[b][t+1].
+inline TokenView lm_tokens(const int32_t* tokens, int T) {
+  return TokenView{tokens, T + 1, tokens + 1, T + 1};
+}
+
+// Number of scored positions of the listed sequences.
+inline int64_t scored_positions(const TokenView& tv, int T, const int* seq_ids, int n_seq) {
+  int64_t n = 0;
+  for (int s = 0; s < n_seq; ++s)
+    for (int t = 0; t < T; ++t) n += tv.targets[int64_t(seq_ids[s]) * tv.tg_stride + t] >= 0 ? 1 : 0;
+  return n;
+}
+
+// Per-sequence loss sums sum_t l_{b,t} over the scored steps, for the requested sequences.
 //   W : weights as the model uses them (already perturbed and rounded), flat layout, type P.
-//   tokens : [B][T+1] int32.
+//   tv : inputs and targets (see TokenView).
 // P is the weight element type (float, double or Dual); S the arithmetic type.
 template <class S, class P>
-void lstm_sequence_losses(const ModelShape& m, const P* W, const int32_t* tokens,
+void lstm_sequence_losses(const ModelShape& m, const P* W, const TokenView& tv,
                           const int* seq_ids, int n_seq, bool round_act_bf16, S* seq_loss_out) {
   using std::exp;
   using std::log;
@@ -121,7 +150,8 @@ void lstm_sequence_losses(const ModelShape& m, const P* W, const int32_t* tokens
   std::vector<S> xin, hin, gates(4 * int64_t(H)), z(V);
   for (int s = 0; s < n_seq; ++s) {
     const int b = seq_ids[s];
-    const int32_t* tok = tokens + int64_t(b) * (T + 1);
+    const int32_t* in_tok = tv.inputs + int64_t(b) * tv.in_stride;
+    const int32_t* tg_tok = tv.targets + int64_t(b) * tv.tg_stride;
     for (int l = 0; l < L; ++l) {
       for (int j = 0; j < H; ++j) {
         h[l][j] = S(0.0);
@@ -133,7 +163,7 @@ void lstm_sequence_losses(const ModelShape& m, const P* W, const int32_t* tokens
       // Layer-0 input: the embedding row of the current token (already in the model's storage
       // precision, so it needs no activation rounding).
       xin.assign(E, S(0.0));
-      for (int e = 0; e < E; ++e) xin[e] = S(emb[int64_t(tok[t]) * E + e]);
+      for (int e = 0; e < E; ++e) xin[e] = S(emb[int64_t(in_tok[t]) * E + e]);
       for (int l = 0; l < L; ++l) {
         const int in = (l == 0) ? E : H;
         const P* w_ih = W + lay[1 + 3 * l].offset;
@@ -161,6 +191,8 @@ void lstm_sequence_losses(const ModelShape& m, const P* W, const int32_t* tokens
         for (int j = 0; j < H; ++j) xin[j] = act_round(h[l][j], round_act_bf16);
       }
       // Logits from the last layer's (rounded) output, then cross-entropy with max subtraction.
+      const int y = tg_tok[t];
+      if (y < 0) continue;  // not scored
       for (int v = 0; v < V; ++v) {
         S acc = S(0.0);
         for (int k = 0; k < H; ++k) acc += S(w_out[int64_t(v) * H + k]) * xin[k];
@@ -173,7 +205,6 @@ void lstm_sequence_losses(const ModelShape& m, const P* W, const int32_t* tokens
       const S zmax = z[vmax];
       S sum = S(0.0);
       for (int v = 0; v < V; ++v) sum += exp(z[v] - zmax);
-      const int y = tok[t + 1];
       total += (zmax + log(sum)) - z[y];
     }
     seq_loss_out[s] = total;

@@ -84,7 +84,11 @@ class Oracle:
             "oracle_sign": (ctypes.c_int, [u64, u32, u32, u32]),
             "oracle_sign_block": (None, [u64, u32, u32, u32, u32, u32, P]),
             "oracle_probe_vector": (None, [P, u64, P]),
+            "oracle_signs_at": (None, [P, u64, P, i64, P]),
             "oracle_lstm_seq_losses": (None, [P, P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P]),
+            "oracle_lstm_seq_losses_io": (None, [P, P, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int, P]),
+            "oracle_probe_losses_io": (None, [P, P, P, P, u64, P, ctypes.c_int, P, ctypes.c_int, P, P]),
+            "oracle_step_io": (ctypes.c_int, [P, P, P, P, u64, P]),
             "oracle_probe_losses": (None, [P, P, P, u64, P, ctypes.c_int, P, ctypes.c_int, P, P]),
             "oracle_update": (ctypes.c_int, [P, P, u64, P, P, i64]),
             "oracle_update_f64losses": (ctypes.c_int, [P, P, u64, P]),
@@ -143,6 +147,14 @@ class Oracle:
         self.lib.oracle_probe_vector(ctypes.byref(c), seed, _ptr(out))
         return out
 
+    def signs_at(self, cfg: OracleConfig, seed: int, elems: np.ndarray) -> np.ndarray:
+        """Signs of probe ``seed`` at flat indices ``elems``, one Philox call per element."""
+        elems = np.ascontiguousarray(elems, np.int64)
+        out = np.zeros(len(elems), dtype=np.int8)
+        c = cfg.c()
+        self.lib.oracle_signs_at(ctypes.byref(c), seed, _ptr(elems), len(elems), _ptr(out))
+        return out
+
     def flat_probe(self, seed: int, d: int) -> np.ndarray:
         out = np.zeros(d, dtype=np.int8)
         self.lib.oracle_flat_probe(seed, d, _ptr(out))
@@ -159,6 +171,40 @@ class Oracle:
                                         _ptr(np.ascontiguousarray(tokens, np.int32)), _ptr(seq_ids),
                                         len(seq_ids), int(round_act_bf16), _ptr(out))
         return out
+
+    def seq_losses_io(self, cfg: OracleConfig, weights: np.ndarray, inputs: np.ndarray, targets: np.ndarray,
+                      seq_ids=None, round_act_bf16: bool = False) -> np.ndarray:
+        storage = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float64): 2}[weights.dtype]
+        seq_ids = np.arange(cfg.batch, dtype=np.int32) if seq_ids is None else np.asarray(seq_ids, np.int32)
+        out = np.zeros(len(seq_ids), dtype=np.float64)
+        c = cfg.c()
+        self.lib.oracle_lstm_seq_losses_io(ctypes.byref(c), _ptr(np.ascontiguousarray(weights)), storage,
+                                           _ptr(np.ascontiguousarray(inputs, np.int32)),
+                                           _ptr(np.ascontiguousarray(targets, np.int32)), _ptr(seq_ids),
+                                           len(seq_ids), int(round_act_bf16), _ptr(out))
+        return out
+
+    def probe_losses_io(self, cfg: OracleConfig, theta: np.ndarray, inputs: np.ndarray, targets: np.ndarray,
+                        step: int, probe_ids=None, seq_ids=None):
+        """Transduction form of probe_losses: inputs [B][T], targets [B][T] (negative: not scored)."""
+        probe_ids = np.arange(cfg.n_probes, dtype=np.int32) if probe_ids is None else np.asarray(probe_ids, np.int32)
+        seq_ids = np.arange(cfg.batch, dtype=np.int32) if seq_ids is None else np.asarray(seq_ids, np.int32)
+        losses = np.zeros(2 * len(probe_ids), dtype=np.float32)
+        seq = np.zeros((2 * len(probe_ids), len(seq_ids)), dtype=np.float64)
+        c = cfg.c()
+        self.lib.oracle_probe_losses_io(ctypes.byref(c), _ptr(np.ascontiguousarray(theta)),
+                                        _ptr(np.ascontiguousarray(inputs, np.int32)),
+                                        _ptr(np.ascontiguousarray(targets, np.int32)), step,
+                                        _ptr(probe_ids), len(probe_ids), _ptr(seq_ids), len(seq_ids),
+                                        _ptr(losses), _ptr(seq))
+        return losses, seq
+
+    def step_io(self, cfg: OracleConfig, theta: np.ndarray, inputs: np.ndarray, targets: np.ndarray, step: int):
+        losses = np.zeros(2 * cfg.n_probes, dtype=np.float32)
+        c = cfg.c()
+        rc = self.lib.oracle_step_io(ctypes.byref(c), _ptr(theta), _ptr(np.ascontiguousarray(inputs, np.int32)),
+                                     _ptr(np.ascontiguousarray(targets, np.int32)), step, _ptr(losses))
+        return losses, int(rc)
 
     def probe_losses(self, cfg: OracleConfig, theta: np.ndarray, tokens: np.ndarray, step: int,
                      probe_ids=None, seq_ids=None):

@@ -70,6 +70,18 @@ void oracle_probe_vector(const oracle_cfg* c, uint64_t seed, int8_t* out) {
   std::memcpy(out, p.data(), p.size());
 }
 
+// Signs of one probe at the listed flat indices of the LSTM layout, each evaluated on its own
+// (one Philox call per element, no reuse between elements), for sampled checks of large models.
+void oracle_signs_at(const oracle_cfg* c, uint64_t seed, const int64_t* elems, int64_t n,
+                     int8_t* out) {
+  const auto lay = lstm_layout(shape_of(c));
+  LayoutIndexer index(lay);
+  for (int64_t q = 0; q < n; ++q) {
+    const ElementIndex e = index.at(elems[q]);
+    out[q] = static_cast<int8_t>(probe_sign(seed, e.tensor, e.row, e.col));
+  }
+}
+
 // Per-sequence loss sums of the unperturbed model. `weights` are in the storage given by
 // `weight_storage` (0 fp32, 1 bf16 bits, 2 double).
 void oracle_lstm_seq_losses(const oracle_cfg* c, const void* weights, int weight_storage,
@@ -79,33 +91,49 @@ void oracle_lstm_seq_losses(const oracle_cfg* c, const void* weights, int weight
   const int64_t d = layout_size(lstm_layout(m));
   std::vector<double> w(d);
   for (int64_t j = 0; j < d; ++j) w[j] = load_param(weights, static_cast<Storage>(weight_storage), j);
-  lstm_sequence_losses<double, double>(m, w.data(), tokens, seq_ids, n_seq, round_act_bf16 != 0, out);
+  lstm_sequence_losses<double, double>(m, w.data(), lm_tokens(tokens, m.T), seq_ids, n_seq,
+                                       round_act_bf16 != 0, out);
+}
+
+// The same with inputs [B][T] and targets [B][T] given separately (a target below zero is not
+// scored): the transduction form.
+void oracle_lstm_seq_losses_io(const oracle_cfg* c, const void* weights, int weight_storage,
+                               const int32_t* inputs, const int32_t* targets, const int* seq_ids,
+                               int n_seq, int round_act_bf16, double* out) {
+  const ModelShape m = shape_of(c);
+  const int64_t d = layout_size(lstm_layout(m));
+  std::vector<double> w(d);
+  for (int64_t j = 0; j < d; ++j) w[j] = load_param(weights, static_cast<Storage>(weight_storage), j);
+  lstm_sequence_losses<double, double>(m, w.data(), TokenView{inputs, m.T, targets, m.T}, seq_ids, n_seq,
+                                       round_act_bf16 != 0, out);
 }
 
 // Probe losses of a subset of probes on a subset of sequences.
-//   losses_out[2k], [2k+1]: mean loss over the selected sequences for probe probe_ids[k] at
-//     +eps and -eps (this is the CD-RGE loss when all B sequences are selected), as float.
-//   seq_out[(2k+side)*n_seq + s]: the per-sequence sum over time of the cross-entropy.
+//   losses_out[2k], [2k+1]: mean loss over the scored positions of the selected sequences for
+//     probe probe_ids[k] at +eps and -eps (this is the CD-RGE loss when all B sequences are
+//     selected), as float.
+//   seq_out[(2k+side)*n_seq + s]: the per-sequence sum over the scored steps of the cross-entropy.
 // theta is in cfg->storage. Activations are rounded to bf16 for bf16 storage.
-void oracle_probe_losses(const oracle_cfg* c, const void* theta, const int32_t* tokens,
-                         uint64_t step, const int* probe_ids, int n_ids, const int* seq_ids,
-                         int n_seq, float* losses_out, double* seq_out) {
+static void probe_losses_view(const oracle_cfg* c, const void* theta, const TokenView& tv,
+                              uint64_t step, const int* probe_ids, int n_ids, const int* seq_ids,
+                              int n_seq, float* losses_out, double* seq_out) {
   const ModelShape m = shape_of(c);
   const auto lay = lstm_layout(m);
   const Storage s = static_cast<Storage>(c->storage);
   const bool round_act = (s == Storage::BF16);
+  const double scored = static_cast<double>(scored_positions(tv, m.T, seq_ids, n_seq));
   std::vector<double> seq(n_seq);
   int side_index = 0;
   auto loss = [&](const auto& w) {
     using P = typename std::decay_t<decltype(w)>::value_type;
-    lstm_sequence_losses<double, P>(m, w.data(), tokens, seq_ids, n_seq, round_act, seq.data());
+    lstm_sequence_losses<double, P>(m, w.data(), tv, seq_ids, n_seq, round_act, seq.data());
     double total = 0.0;
     for (int q = 0; q < n_seq; ++q) {
       total += seq[q];
       if (seq_out) seq_out[int64_t(side_index) * n_seq + q] = seq[q];
     }
     ++side_index;
-    return total / (static_cast<double>(n_seq) * m.T);
+    return total / scored;
   };
   std::vector<double> out(2 * int64_t(n_ids));
   if (s == Storage::F64) {
@@ -117,6 +145,22 @@ void oracle_probe_losses(const oracle_cfg* c, const void* theta, const int32_t* 
                                 out.data());
   }
   for (int64_t q = 0; q < 2 * int64_t(n_ids); ++q) losses_out[q] = static_cast<float>(out[q]);
+}
+
+// Language-model form: tokens [B][T+1], every position scored.
+void oracle_probe_losses(const oracle_cfg* c, const void* theta, const int32_t* tokens,
+                         uint64_t step, const int* probe_ids, int n_ids, const int* seq_ids,
+                         int n_seq, float* losses_out, double* seq_out) {
+  probe_losses_view(c, theta, lm_tokens(tokens, c->seq_len), step, probe_ids, n_ids, seq_ids, n_seq,
+                    losses_out, seq_out);
+}
+
+// Transduction form: inputs [B][T], targets [B][T] (below zero: not scored).
+void oracle_probe_losses_io(const oracle_cfg* c, const void* theta, const int32_t* inputs,
+                            const int32_t* targets, uint64_t step, const int* probe_ids, int n_ids,
+                            const int* seq_ids, int n_seq, float* losses_out, double* seq_out) {
+  probe_losses_view(c, theta, TokenView{inputs, c->seq_len, targets, c->seq_len}, step, probe_ids,
+                    n_ids, seq_ids, n_seq, losses_out, seq_out);
 }
 
 // The CD-RGE update in place over all elements (elems null) or the listed flat indices.
@@ -146,6 +190,17 @@ int oracle_step(const oracle_cfg* c, void* theta, const int32_t* tokens, uint64_
   return oracle_update(c, theta, step, losses_out, nullptr, 0);
 }
 
+// Full CD-RGE step in the transduction form.
+int oracle_step_io(const oracle_cfg* c, void* theta, const int32_t* inputs, const int32_t* targets,
+                   uint64_t step, float* losses_out) {
+  std::vector<int> probes(c->n_probes), seqs(c->batch);
+  for (int i = 0; i < c->n_probes; ++i) probes[i] = i;
+  for (int b = 0; b < c->batch; ++b) seqs[b] = b;
+  oracle_probe_losses_io(c, theta, inputs, targets, step, probes.data(), c->n_probes, seqs.data(),
+                         c->batch, losses_out, nullptr);
+  return oracle_update(c, theta, step, losses_out, nullptr, 0);
+}
+
 // Loss and its exact directional derivative along `direction` (forward-mode dual numbers) for
 // exact (double) weights, over all sequences.
 void oracle_lstm_dir_deriv(const oracle_cfg* c, const double* theta, const int32_t* tokens,
@@ -157,7 +212,7 @@ void oracle_lstm_dir_deriv(const oracle_cfg* c, const double* theta, const int32
   std::vector<int> ids(m.B);
   for (int b = 0; b < m.B; ++b) ids[b] = b;
   std::vector<Dual> seq(m.B);
-  lstm_sequence_losses<Dual, Dual>(m, w.data(), tokens, ids.data(), m.B, false, seq.data());
+  lstm_sequence_losses<Dual, Dual>(m, w.data(), lm_tokens(tokens, m.T), ids.data(), m.B, false, seq.data());
   Dual total(0.0);
   for (int b = 0; b < m.B; ++b) total += seq[b];
   const double scale = 1.0 / (static_cast<double>(m.B) * m.T);

@@ -169,3 +169,106 @@ def test_bf16_probe_losses_match_torch(oracle):
             pert = (w32 + torch.tensor(sgn * cfg.eps, dtype=torch.float32) * p).to(torch.bfloat16)
             ref = torch_bf16_seq_losses(oracle, cfg, pert.to(torch.float64).numpy(), tokens)
             np.testing.assert_allclose(seq[2 * i + side], ref, rtol=1e-12, atol=0)
+
+
+def test_fp32_probe_losses_match_torch(oracle):
+    """Perturbed fp32 forwards: theta' = fl32(w + s eps p) formed by torch in float32 (one
+    rounding of the sum; s eps p is exact) from the oracle's probe vector, then torch's LSTM in
+    float64 on those float32 values. Covers the fp32 branch of the oracle's perturbed copy. eps is
+    large enough that leaving any one tensor unperturbed moves the losses far beyond 1e-12."""
+    shape = SHAPES[1]
+    cfg = OracleConfig(n_probes=2, storage="f32", eps=3e-2, lr=3e-2, base_seed=78, **shape)
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(25)
+    w32 = rng.uniform(-0.3, 0.3, d).astype(np.float32)
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    step = 3
+    _, seq = oracle.probe_losses(cfg, w32, tokens, step)
+    w = torch.from_numpy(w32)
+    lay = oracle.layout(cfg)
+    for i in range(cfg.n_probes):
+        p = torch.from_numpy(oracle.probe_vector(cfg, oracle.probe_seed(cfg.base_seed, step, i)).astype(np.float32))
+        for side, sgn in enumerate((1.0, -1.0)):
+            pert = w + torch.tensor(sgn * cfg.eps, dtype=torch.float32) * p
+            assert pert.dtype == torch.float32
+            ref = torch_seq_losses(oracle, cfg, pert.to(torch.float64).numpy(), tokens)
+            np.testing.assert_allclose(seq[2 * i + side], ref, rtol=1e-12, atol=0)
+            # every tensor's perturbation is visible at this bar
+            for tid, off, rows, cols in lay:
+                part = pert.clone()
+                part[off:off + rows * cols] = w[off:off + rows * cols]
+                moved = torch_seq_losses(oracle, cfg, part.to(torch.float64).numpy(), tokens)
+                assert np.max(np.abs(moved - ref) / np.abs(ref)) > 1e-9, tid
+
+
+def torch_io_seq_losses(oracle, cfg, theta64, inputs, targets):
+    """torch's LSTM on separate inputs [B][T]; cross-entropy against targets [B][T] with
+    ignore_index=-1 (ignored positions add nothing). Returns per-sequence sums and the mean over
+    the scored positions (torch's own 'mean' reduction)."""
+    lay = {tid: (off, rows, cols) for tid, off, rows, cols in oracle.layout(cfg)}
+
+    def tensor(tid):
+        off, rows, cols = lay[tid]
+        return torch.from_numpy(theta64[off:off + rows * cols].reshape(rows, cols).copy())
+
+    L, H = cfg.n_layers, cfg.hidden
+    lstm = torch.nn.LSTM(cfg.embed, H, num_layers=L, batch_first=True, dtype=torch.float64)
+    with torch.no_grad():
+        for l in range(L):
+            getattr(lstm, f"weight_ih_l{l}").copy_(tensor(1 + 3 * l))
+            getattr(lstm, f"weight_hh_l{l}").copy_(tensor(2 + 3 * l))
+            getattr(lstm, f"bias_ih_l{l}").copy_(tensor(3 + 3 * l).reshape(-1))
+            getattr(lstm, f"bias_hh_l{l}").zero_()
+        x = tensor(0)[torch.from_numpy(inputs.astype(np.int64))]
+        out, _ = lstm(x)
+        logits = torch.nn.functional.linear(out, tensor(1 + 3 * L), tensor(2 + 3 * L).reshape(-1))
+        tg = torch.from_numpy(targets.astype(np.int64)).reshape(-1)
+        flat = logits.reshape(-1, cfg.vocab)
+        ce = torch.nn.functional.cross_entropy(flat, tg, ignore_index=-1, reduction="none")
+        mean = torch.nn.functional.cross_entropy(flat, tg, ignore_index=-1, reduction="mean")
+        return ce.reshape(cfg.batch, cfg.seq_len).sum(dim=1).numpy(), float(mean)
+
+
+def test_io_form_matches_torch_with_ignored_targets(oracle):
+    """The transduction form: inputs and targets given separately, targets of -1 not scored, the
+    loss the mean over the scored positions. Pinned to torch's cross_entropy with ignore_index;
+    the perturbed losses of probe_losses_io to the same torch model on a perturbed copy formed in
+    torch from the oracle's probe vector (fp32 storage)."""
+    shape = SHAPES[1]
+    cfg = OracleConfig(n_probes=2, storage="f32", eps=3e-2, lr=3e-2, base_seed=79, **shape)
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(26)
+    w32 = rng.uniform(-0.4, 0.4, d).astype(np.float32)
+    B, T, V = cfg.batch, cfg.seq_len, cfg.vocab
+    inputs = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    targets = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    targets[rng.random((B, T)) < 0.4] = -1
+    targets[0, :] = -1                                   # a sequence with nothing scored
+    targets[1, :] = rng.integers(0, V, size=T)           # one with everything scored
+    got = oracle.seq_losses_io(cfg, w32, inputs, targets)
+    ref, _ = torch_io_seq_losses(oracle, cfg, w32.astype(np.float64), inputs, targets)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-300)
+    assert got[0] == 0.0
+    step = 4
+    losses, seq = oracle.probe_losses_io(cfg, w32, inputs, targets, step)
+    w = torch.from_numpy(w32)
+    for i in range(cfg.n_probes):
+        p = torch.from_numpy(oracle.probe_vector(cfg, oracle.probe_seed(cfg.base_seed, step, i)).astype(np.float32))
+        for side, sgn in enumerate((1.0, -1.0)):
+            pert = (w + torch.tensor(sgn * cfg.eps, dtype=torch.float32) * p).to(torch.float64).numpy()
+            ref_seq, ref_mean = torch_io_seq_losses(oracle, cfg, pert, inputs, targets)
+            np.testing.assert_allclose(seq[2 * i + side], ref_seq, rtol=1e-12, atol=1e-300)
+            assert losses[2 * i + side] == np.float32(ref_mean)
+
+
+def test_lm_form_is_the_io_form_with_shifted_targets(oracle):
+    shape = SHAPES[0]
+    cfg = OracleConfig(n_probes=2, storage="bf16", eps=1e-2, lr=1e-2, base_seed=80, **shape)
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(27)
+    w16 = _bf16_bits(rng.uniform(-0.3, 0.3, d))
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    a = oracle.probe_losses(cfg, w16, tokens, 1)
+    b = oracle.probe_losses_io(cfg, w16, tokens[:, :-1].copy(), tokens[:, 1:].copy(), 1)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])

@@ -74,3 +74,48 @@ def test_mapping_uses_every_bit_once(oracle):
     a = oracle.sign_block(seed, 5, 0, 64, 0, 128).astype(np.float64)
     b = oracle.sign_block(seed, 5, 0, 64, 128, 128).astype(np.float64)
     assert abs((a * b).mean()) < 5 / np.sqrt(a.size)
+
+
+# A layout whose rows cross 128-column Philox blocks (W_ih of layer 0 has 200 columns) and whose
+# tensors are of every kind (embedding, matrices, biases, output layer).
+_LAYOUT_CFG = OracleConfig(2, 7, 200, 40, 1, 1, 5, "f32", 1e-3, 1e-3, 3117)
+
+
+def test_probe_vector_matches_uncached_sign(oracle):
+    """probe_vector walks rows through a reader that keeps the last Philox block; every element
+    must equal the uncached probe_sign (pinned to rocRAND above), evaluated element by element."""
+    cfg = _LAYOUT_CFG
+    d = oracle.param_count(cfg)
+    every = np.arange(d, dtype=np.int64)
+    for step, i in [(0, 0), (0, 4), (9, 2)]:
+        seed = oracle.probe_seed(cfg.base_seed, step, i)
+        np.testing.assert_array_equal(oracle.probe_vector(cfg, seed), oracle.signs_at(cfg, seed, every))
+    # and per tensor through the rectangular block reader, which is also uncached
+    seed = oracle.probe_seed(cfg.base_seed, 3, 1)
+    vec = oracle.probe_vector(cfg, seed)
+    for tid, off, rows, cols in oracle.layout(cfg):
+        blk = oracle.sign_block(seed, tid, 0, rows, 0, cols)
+        np.testing.assert_array_equal(vec[off:off + rows * cols], blk.reshape(-1))
+
+
+def test_update_reads_uncached_signs(oracle):
+    """The update keeps one cached reader per probe; with theta = 0 and d = e_i the updated theta
+    is -coef * p_i exactly (coef = 1/(2K) at eta = eps), for all elements in order and for a
+    shuffled subset of elements (the reader and the layout walk then jump between tensors)."""
+    cfg = _LAYOUT_CFG
+    d = oracle.param_count(cfg)
+    coef = 1.0 / (2 * cfg.n_probes)
+    rng = np.random.default_rng(3)
+    subset = rng.permutation(d)[: d // 3].astype(np.int64)
+    for i in (0, 3):
+        losses = np.zeros(2 * cfg.n_probes, np.float32)
+        losses[2 * i] = 1.0
+        seed = oracle.probe_seed(cfg.base_seed, 4, i)
+        theta = np.zeros(d, np.float32)
+        assert oracle.update(cfg, theta, 4, losses) == 0
+        np.testing.assert_array_equal(theta, -coef * oracle.signs_at(cfg, seed, np.arange(d)).astype(np.float32))
+        part = np.zeros(d, np.float32)
+        assert oracle.update(cfg, part, 4, losses, elems=subset) == 0
+        np.testing.assert_array_equal(part[subset], -coef * oracle.signs_at(cfg, seed, subset).astype(np.float32))
+        rest = np.setdiff1d(np.arange(d), subset)
+        assert not part[rest].any()
