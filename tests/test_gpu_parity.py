@@ -5,11 +5,15 @@ tile, several 64-unit row tiles, two layers, probe chunks of unequal size; fp32 
 two workgroups, two probe pairs per workgroup with an odd pair count, more gate rows than threads,
 inputs that are not a multiple of 32 columns. Bars: probe seeds and signs bit-exact; losses and per-sequence losses within
 1e-5 (fp32) or 2e-2 (bf16) relative; updated parameters within the same bars normwise per tensor.
+For bf16, whose 2e-2 bar is far wider than what a probe moves a loss, the differences
+L(theta + eps p_i) - L(theta - eps p_i) per sequence and per probe are held to the probe-difference
+bar of parity_bars.py, and cases with a large eps (or theta = 0) make the probe dominate the loss.
 """
 import numpy as np
 import pytest
 
 from gpu_util import HipRun, TOL, as_f64, assert_losses_close, assert_theta_close, dtype_name, ocfg, say
+from parity_bars import PROBE_CASES, assert_diffs_close, probe_case_inputs
 from zero_order_recurrent_amd import binding as b
 from zero_order_recurrent_amd.inputs import PRESETS, make_theta, make_tokens, to_bf16_bits
 
@@ -60,6 +64,10 @@ def test_small_step_parity(oracle, name):
     ref_l, ref_seq = oracle.probe_losses(oc, theta, tokens, 2)
     assert_losses_close(losses, ref_l, tol)
     assert_losses_close(seq, ref_seq, tol, "seq_losses")
+    if c.dtype == b.CDRGE_BF16:
+        e = assert_diffs_close(seq, ref_seq)
+        assert_diffs_close(losses[:, None], ref_l[:, None], "per-probe d_i")
+        say(f"    probe differences at {max(e):.3f} x the bar")
     # the per-probe reduction: loss = sum_b seq / (B T)
     np.testing.assert_allclose(losses, seq.astype(np.float64).sum(1) / (c.batch * c.seq_len), rtol=1e-6)
     assert run.update(2) == 0
@@ -291,5 +299,32 @@ def test_xcd_grouped_tile_order(oracle, hidden, pairs):
     ref_l, ref_seq = oracle.probe_losses(ocfg(c), theta, tokens, 0, probe_ids=probes, seq_ids=seqs)
     rows = [2 * i + s for i in probes for s in (0, 1)]
     assert_losses_close(seq[np.ix_(rows, seqs)], ref_seq, 2e-2, "seq_losses")
+    assert_diffs_close(seq[np.ix_(rows, seqs)], ref_seq)
     np.testing.assert_allclose(losses, seq.astype(np.float64).sum(1) / (c.batch * c.seq_len), rtol=1e-6)
+    run.close()
+
+
+@pytest.mark.parametrize("name", list(PROBE_CASES))
+def test_probe_dominant_bf16(oracle, name):
+    # eps = 2^-3 .. 2^-7 against weights of 1/sqrt(H) (or theta = 0): the probe moves the losses by
+    # 0.5-10%, and the differences d_i must match the oracle's within the probe-difference bar
+    L, V, E, H, B, T, K, eps, base, ppc, zero = PROBE_CASES[name]
+    c = b.make_config(L, V, E, H, B, T, K, "bf16", eps, eps, base, probes_per_chunk=ppc)
+    say(f"[gpu] probe-dominant bf16 {name}")
+    theta32, tokens = probe_case_inputs(PROBE_CASES[name])
+    theta = to_bf16_bits(theta32)
+    run = HipRun(c, theta, tokens)
+    losses, seq, st = run.probe_losses(step=2)
+    assert st == 0
+    oc = ocfg(c)
+    ref_l, ref_seq = oracle.probe_losses(oc, theta, tokens, 2)
+    assert_losses_close(losses, ref_l, 2e-2)
+    assert_losses_close(seq, ref_seq, 2e-2, "seq_losses")
+    e = assert_diffs_close(seq, ref_seq)
+    assert_diffs_close(losses[:, None], ref_l[:, None], "per-probe d_i")
+    say(f"    probe differences at {max(e):.3f} x the bar")
+    assert run.update(2) == 0
+    ref_theta = theta.copy()
+    assert oracle.update(oc, ref_theta, 2, ref_l) == 0
+    assert_theta_close(oracle, c, run.theta(), ref_theta, 2e-2)
     run.close()
