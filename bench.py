@@ -3,16 +3,21 @@
 
 A step is the whole hot path on one batch: 2K perturbed LSTM forward passes with per-probe
 cross-entropy losses (cdrge_probe_losses), then the seed-regenerating update (cdrge_update).
-The default workload is the character-level LM of the pages' runtime table setting
-(batch 1,024, training length 10, character vocabulary): 2-layer LSTM, E = 128, H = 1024, V = 50,
-bf16 weights with fp32 accumulation, K = 64 probe pairs, eps = eta = 1e-4, Zipf(1.1) tokens.
+The default workload is the largest one that fits one GPU, the ~1.1B-parameter model: 4-layer
+LSTM, E = H = 5888, V = 50, bf16 weights with fp32 accumulation, batch 256, sequence length 10,
+K = 16 probe pairs evaluated in chunks of 8, eps = eta = 1e-4, Zipf(1.1) tokens. --workload
+selects the others (tiny, overfit, charlm, lstm270m).
 
 Printed JSON line:
   value        perturbed-forward tokens per second over whole steps, 2K * B * T / step time
   roofline     the recurrent gate kernel (the dominant kernel): algorithmic matrix-core flops
                per launch / mean launch duration from HIP events on the launch stream, against
                the bf16 dense MFMA peak
-  cpu_baseline the plain single-threaded CPU oracle on a bounded sample of the same workload
+  update_roofline  the update kernel against HBM (algorithmic bytes / launch time), with its
+               ALU issue floor next to it
+  cpu_baseline the plain single-threaded CPU oracle on a bounded sample of the same workload: on
+               one core and as independent processes on the host's cores, with the CPU model
+               and an extrapolated full-step time
 """
 from __future__ import annotations
 
@@ -64,27 +69,172 @@ def traffic_from_profiles(kernel_tag: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(preset, theta, tokens, budget_s: float):
-    """Times the oracle on one probe pair over as many sequences as fit in about budget_s."""
-    from oracle import Oracle, OracleConfig
+def cpu_info() -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
+
+
+def _mem_available() -> int:
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return 0
+
+
+def _oracle_config(preset):
+    from oracle import OracleConfig
+    return OracleConfig(preset.n_layers, preset.vocab, preset.embed, preset.hidden, preset.batch,
+                        preset.seq_len, preset.n_probes, preset.dtype, preset.eps, preset.lr, preset.base_seed)
+
+
+def cpu_worker(args) -> None:
+    """Child process of the all-cores leg: one probe pair (both signs) over its own sequences."""
+    from oracle import Oracle
+    from zero_order_recurrent_amd.inputs import PRESETS
+    theta = np.load(os.path.join(args.cpu_worker, "theta.npy"), mmap_mode="r")
+    tokens = np.load(os.path.join(args.cpu_worker, "tokens.npy"))
+    p = PRESETS[args.workload].with_(seq_len=tokens.shape[1] - 1)
     o = Oracle()
-    oc = OracleConfig(preset.n_layers, preset.vocab, preset.embed, preset.hidden, preset.batch,
-                      preset.seq_len, preset.n_probes, preset.dtype, preset.eps, preset.lr, preset.base_seed)
-    # the call's cost is a fixed part (the perturbed parameter copies) plus a per-sequence part
-    def timed(n):
+    seqs = [int(v) for v in args.worker_seqs.split(",")]
+    t0 = time.perf_counter()
+    o.probe_losses(_oracle_config(p), theta, tokens, 0, probe_ids=[args.worker_probe], seq_ids=seqs)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"seconds": dt, "tokens": 2 * len(seqs) * p.seq_len}), flush=True)
+
+
+def cpu_baseline(preset, theta, tokens, budget_s: float) -> dict:
+    """The oracle (plain single-threaded C++) on the host's cores, on a bounded sample of the
+    workload: one probe pair, both signs, over full sequences, at full model shape, including the
+    perturbed parameter copies the oracle builds for each sign.
+
+    1 core: the copies alone (0 sequences) and then with n sequences give the fixed cost per
+    perturbed model and the cost per sequence; with the oracle's update timed on a slice of
+    parameters, they extrapolate a whole CD-RGE step (2K perturbed models x B sequences + update).
+    All cores: independent oracle processes over disjoint (probe pair, sequence) slices, as many
+    as the host's cores (at most 16) and its free memory (one perturbed copy per process) allow.
+    """
+    import subprocess
+    import tempfile
+    from oracle import Oracle
+    o = Oracle()
+    oc = _oracle_config(preset)
+    d = theta.size
+
+    def timed(probe, seqs):
         t0 = time.perf_counter()
-        o.probe_losses(oc, theta, tokens, 0, probe_ids=[0], seq_ids=list(range(n)))
+        o.probe_losses(oc, theta, tokens, 0, probe_ids=[probe], seq_ids=list(seqs))
         return time.perf_counter() - t0
-    n_probe = min(4, preset.batch)
-    t1, tn = timed(1), timed(n_probe)
-    per_seq = max((tn - t1) / max(n_probe - 1, 1), 1e-4)
-    fixed = max(t1 - per_seq, 0.0)
-    n_seq = int(max(1, min(preset.batch, (budget_s - fixed) / per_seq)))
-    dt = timed(n_seq)
-    toks = 2 * n_seq * preset.seq_len
-    return {"value": toks / dt, "unit": "perturbed-forward tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"probe pair 0 (both signs) x {n_seq} sequences x T={preset.seq_len} at full model "
-                      f"shape, including the perturbed parameter copies; {dt:.1f} s"}
+
+    t_copies = timed(0, [])                      # two perturbed copies, no forward
+    t_one = timed(0, [0])                        # the copies and one sequence per sign
+    per_seq = max((t_one - t_copies) / 2, 1e-6)  # one sequence through one perturbed model
+    per_copy = t_copies / 2
+    n_seq = int(max(1, min(preset.batch, (budget_s - t_copies) / (2 * per_seq))))
+    dt = t_one if n_seq == 1 else timed(0, range(n_seq))
+    single = {"value": 2 * n_seq * preset.seq_len / dt, "cores": 1, "seconds": dt,
+              "sample": f"probe pair 0 (both signs) x {n_seq} sequence(s) x T={preset.seq_len} at full model "
+                        f"shape, including the two perturbed parameter copies"}
+    # the update on the first parameters (a full-length buffer of which only that slice is ever
+    # touched, since the oracle updates listed elements in place), scaled to d
+    n_upd = int(min(d, 1 << 21))
+    work = np.empty(d, dtype=theta.dtype)
+    work[:n_upd] = theta[:n_upd]
+    losses = (3.0 + 1e-3 * np.random.default_rng(0).standard_normal(2 * preset.n_probes)).astype(np.float32)
+    t0 = time.perf_counter()
+    o.update(oc, work, 0, losses, elems=None if n_upd == d else np.arange(n_upd, dtype=np.int64))
+    t_upd = (time.perf_counter() - t0) * d / n_upd
+    del work
+    models = 2 * preset.n_probes
+    step_1core = models * per_copy + models * preset.batch * per_seq + t_upd
+    single["extrapolated_full_step_s"] = step_1core
+    single["extrapolation"] = (f"extrapolated, not measured: {models} perturbed copies x {per_copy:.3g} s + "
+                               f"{models} x {preset.batch} sequences x {per_seq:.3g} s + update "
+                               f"{t_upd:.3g} s (timed on {n_upd} of {d} parameters)")
+
+    # all cores: disjoint (probe pair, sequences) slices in child processes
+    info = cpu_info()
+    per_proc_bytes = 4 * d + (256 << 20)
+    mem_cap = max(1, int(0.6 * _mem_available() // per_proc_bytes)) if _mem_available() else 1
+    workers = max(1, min(info["nproc"], 16, mem_cap, preset.n_probes * preset.batch))
+    n_each = max(1, min(n_seq, preset.batch * preset.n_probes // workers))
+    allcores = None
+    if workers > 1:
+        tmp = tempfile.mkdtemp(prefix="cdrge_cpu_")
+        try:
+            np.save(os.path.join(tmp, "theta.npy"), theta)
+            np.save(os.path.join(tmp, "tokens.npy"), tokens)
+            procs = []
+            t0 = time.perf_counter()
+            for w in range(workers):
+                probe = w % preset.n_probes
+                first = (w // preset.n_probes) * n_each
+                seqs = ",".join(str((first + q) % preset.batch) for q in range(n_each))
+                procs.append(subprocess.Popen(
+                    [sys.executable, os.path.abspath(__file__), "--workload", preset.name, "--cpu-worker", tmp,
+                     "--worker-probe", str(probe), "--worker-seqs", seqs],
+                    stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+            outs = []
+            for pr in procs:
+                out, err = pr.communicate()
+                if pr.returncode != 0:
+                    raise RuntimeError(f"oracle worker failed ({pr.returncode}): {err[-400:]}")
+                outs.append(json.loads(out.strip().splitlines()[-1]))
+            wall = time.perf_counter() - t0
+        finally:
+            for name in ("theta.npy", "tokens.npy"):
+                try:
+                    os.remove(os.path.join(tmp, name))
+                except OSError:
+                    pass
+            os.rmdir(tmp)
+        toks = sum(r["tokens"] for r in outs)
+        speedup = (toks / wall) / single["value"]
+        allcores = {"value": toks / wall, "cores": workers, "seconds": wall,
+                    "sample": f"{workers} oracle processes, each one probe pair (both signs) x {n_each} "
+                              f"sequence(s) x T={preset.seq_len} at full model shape with its own perturbed "
+                              f"copies; disjoint (probe, sequence) slices",
+                    "extrapolated_full_step_s": step_1core / speedup,
+                    "extrapolation": f"extrapolated, not measured: the 1-core step divided by the measured "
+                                     f"speed-up of {speedup:.2f} on {workers} processes"}
+    best = allcores if allcores is not None else single
+    out = {"value": best["value"], "unit": "perturbed-forward tokens/s", "cores": best["cores"], "kind": "oracle",
+           "sample": best["sample"] + f"; {best['seconds']:.1f} s",
+           "extrapolated_full_step_s": best["extrapolated_full_step_s"],
+           "single_core": single, **info}
+    if allcores is not None:
+        out["all_cores"] = allcores
+    return out
+
+
+def update_alu_floor(workload: str, kernel_ms: float):
+    """The update's issue floor from its committed VALU instruction count (rocprofv3 --pmc
+    SQ_INSTS_VALU, per launch): a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles, so
+    the launch needs at least insts * 4 / (1,024 SIMDs * 2.4 GHz). None unless the counter summary
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"update_{workload}_valu.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    insts = rec["valu_insts_per_launch"]
+    floor_ms = insts * 4 / (1024 * 2.4e9) * 1e3
+    return {"bound": "alu", "valu_insts_per_launch": insts, "floor_ms": floor_ms, "measured_ms": kernel_ms,
+            "frac": floor_ms / kernel_ms if kernel_ms > 0 else None,
+            "peak": "1,024 SIMDs x 2.4 GHz, one wave64 VALU instruction per SIMD per 4 cycles"}
 
 
 def main():
@@ -92,12 +242,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="charlm")
+    ap.add_argument("--workload", default="lstm1b")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="override the workload's sequence length T (same model, batch and probes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--worker-probe", type=int, default=0, help=argparse.SUPPRESS)
+    ap.add_argument("--worker-seqs", default="0", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_worker:
+        cpu_worker(args)
+        return
     if args.calibrate_copy:
         import torch
         n = 1 << 28  # float32 elements: 1 GiB per direction
@@ -113,28 +271,36 @@ def main():
               "is described, not built). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    from zero_order_recurrent_amd import binding as b
     from zero_order_recurrent_amd.inputs import PRESETS, make_theta, make_tokens
 
     p = PRESETS[args.workload]
+    if args.seq_len > 0:
+        p = p.with_(seq_len=args.seq_len)
+    theta_host = make_theta(p, _param_count(p))
+    tokens_host = make_tokens(p)
+    # The CPU legs run first, before this process touches the GPU: the all-cores leg starts
+    # child processes, and the GPU then sits idle rather than sharing the host with them.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(p, theta_host, tokens_host, args.cpu_budget)
+
+    import torch
+    from zero_order_recurrent_amd import binding as b
+
     cfg = b.config_from_preset(p)
     d = b.cdrge_param_count(cfg)
-    theta_host = make_theta(p, d)
-    tokens_host = make_tokens(p)
+    assert d == theta_host.size
     if p.dtype == "bf16":
         params = torch.from_numpy(theta_host.view(np.int16).copy()).cuda()
     else:
         params = torch.from_numpy(theta_host.copy()).cuda()
     tokens = torch.from_numpy(tokens_host).cuda()
     ctx = b.Context(cfg, params)
-    stream = torch.cuda.current_stream()
 
     for s in range(args.warmup):
         ctx.step(tokens, s)
     st = ctx.sync_status()
-    if st not in (0, 5):
-        raise RuntimeError(f"warmup failed: {b.STATUS[st]}")
+    if st != 0:
+        print(f"warmup steps ended with {b.STATUS[st]}", file=sys.stderr)
+        sys.exit(1)
 
     b.cdrge_get_timing(ctx.ctx, 0, reset=True)
     b.cdrge_set_timing(ctx.ctx, True)
@@ -148,6 +314,10 @@ def main():
     work = {k: b.cdrge_get_work(ctx.ctx, k) for k in range(4)}
     timing = {k: b.cdrge_get_timing(ctx.ctx, k) for k in range(4)}
     st = ctx.sync_status()
+    if st != 0:
+        # a non-finite loss turns every update into a no-op: the timings would not be of the path
+        print(f"timed steps ended with {b.STATUS[st]}; no throughput is reported", file=sys.stderr)
+        sys.exit(1)
 
     # A separate forward-only pass (same inputs) for the perturbed-forward rate on its own.
     torch.cuda.synchronize()
@@ -186,8 +356,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "n_layers": p.n_layers, "embed": p.embed, "hidden": p.hidden,
                    "vocab": p.vocab, "batch": p.batch, "seq_len": p.seq_len, "n_probes": p.n_probes,
-                   "eps": p.eps, "lr": p.lr, "params": d, "tokens": p.tokens},
+                   "probes_per_chunk": p.probes_per_chunk, "eps": p.eps, "lr": p.lr, "params": d,
+                   "tokens": p.tokens},
         "cdrge_steps_per_sec": 1.0 / step_s,
+        "ms_per_timestep": step_s * 1e3 / p.seq_len,
+        "workspace_bytes": b.cdrge_workspace_bytes(cfg),
         "forward_only_tokens_per_sec": tokens_per_step / fwd_s,
         "roofline": {"bound": "mfma" if p.dtype == "bf16" else "alu", "kernel": "k_lstm_gates_bf16"
                      if p.dtype == "bf16" else "k_lstm_f32",
@@ -197,17 +370,26 @@ def main():
         "update_roofline": {"bound": "hbm", "kernel": "k_update_perm" if p.dtype == "bf16" and p.n_probes <= 64
                             else "k_update_lut", "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
                             "frac": upd_gbs / PEAK["hbm_gbs"], "traffic": upd_traffic, "launches": upd_n,
-                            "total_ms_per_step": upd_ms / args.steps},
+                            "total_ms_per_step": upd_ms / args.steps,
+                            "alu": update_alu_floor(args.workload, upd_ms / max(upd_n, 1))},
         "time_split_ms_per_step": {"gates": gate_ms / args.steps, "logits_ce": ce_ms / args.steps,
                                    "update": upd_ms / args.steps, "prep": timing[3][0] / args.steps},
         "status": b.STATUS[st],
         "kernel_source_hash": kernel_source_hash(),
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(p, theta_host, tokens_host, args.cpu_budget)
-        line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / line["cpu_baseline"]["value"]
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+        line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / cpu["value"]
     ctx.close()
     print(json.dumps(line), flush=True)
+
+
+def _param_count(p) -> int:
+    """d of the flat layout (embedding, per layer W_ih, W_hh and one bias, output layer)."""
+    d = p.vocab * p.embed + p.vocab * p.hidden + p.vocab
+    for l in range(p.n_layers):
+        d += 4 * p.hidden * (p.embed if l == 0 else p.hidden) + 4 * p.hidden * p.hidden + 4 * p.hidden
+    return d
 
 
 if __name__ == "__main__":
