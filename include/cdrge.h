@@ -159,6 +159,25 @@ cdrge_status cdrge_get_timing(cdrge_ctx* ctx, int kind, double* total_ms, int64_
  * for kind 2. */
 cdrge_status cdrge_get_work(cdrge_ctx* ctx, int kind, double* work);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): one whole step, as cdrge_step, with no context and no
+ * caller workspace. The workspace lives in a static device array of the library, one per device
+ * (held from library load until the process ends), of cdrge_noalloc_max_workspace_bytes()
+ * bytes (64 MiB): configurations whose cdrge_workspace_bytes exceed it are rejected with
+ * CDRGE_ERR_WORKSPACE before anything is enqueued (smaller probes_per_chunk shrinks the need).
+ * The call allocates nothing: no hipMalloc, no hipFree, no library allocation of device memory.
+ * params, tokens and losses are as for cdrge_init, cdrge_probe_losses and cdrge_step; stream is a
+ * hipStream_t (NULL: the default stream). Every call on one device shares that device's array and
+ * finds it as the previous call left it (the status words are cleared at the start of each call),
+ * so calls that overlap on one device - on two streams, or from two threads - race and must be
+ * ordered by the caller. A non-finite loss leaves theta unchanged; with no context, the caller
+ * reads that from the losses it gets back. */
+cdrge_status cdrge_step_noalloc(const cdrge_config* cfg, void* params, const int32_t* tokens,
+                                uint64_t step, float* losses, void* stream);
+
+/* Size in bytes of the static per-device scratch cdrge_step_noalloc uses. */
+size_t cdrge_noalloc_max_workspace_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,3 +99,21 @@ def test_workspace_flat_in_sequence_length(lib):
 def test_status_strings(lib):
     for k, v in b.STATUS.items():
         assert b.cdrge_status_string(k) == v
+
+
+def test_noalloc_entry_point_rejects_before_any_device_work(lib):
+    # 64 MiB of static scratch per device; configurations that need more are refused with
+    # CDRGE_ERR_WORKSPACE (and a message) before the library touches a device, as are null pointers.
+    assert b.cdrge_noalloc_max_workspace_bytes() == 64 << 20
+    big = b.config_from_preset(PRESETS["charlm"])
+    assert b.cdrge_workspace_bytes(big) > 64 << 20
+    fake = b.ctypes.c_void_p(1 << 20)  # never dereferenced: the call returns first
+    st = lib.cdrge_step_noalloc(b.ctypes.byref(big), fake, fake, 0, fake, None)
+    assert st == 3
+    assert "static scratch holds 67108864" in b.cdrge_last_error_detail()
+    small = b.config_from_preset(PRESETS["tiny"])
+    assert b.cdrge_workspace_bytes(small) <= 64 << 20
+    assert lib.cdrge_step_noalloc(b.ctypes.byref(small), None, fake, 0, fake, None) == 1
+    # the largest probe chunk of the char-LM shape that fits
+    fits = b.make_config(2, 50, 128, 1024, 1024, 10, 64, "bf16", 1e-4, 1e-4, 3003, probes_per_chunk=1)
+    assert b.cdrge_workspace_bytes(fits) <= 64 << 20

@@ -67,6 +67,9 @@ EXPORTS = {
     "cdrge_get_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int]),
     "cdrge_get_work": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
+    "cdrge_step_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                          ctypes.c_void_p, ctypes.c_void_p]),
+    "cdrge_noalloc_max_workspace_bytes": (ctypes.c_size_t, []),
 }
 
 
@@ -91,7 +94,7 @@ def lib():
 
 def _check(status: int, where: str):
     if status != 0:
-        detail = lib().cdrge_last_error_detail().decode() if status == 4 else ""
+        detail = lib().cdrge_last_error_detail().decode() if status in (3, 4) else ""
         raise CdrgeError(status, f"{where} {detail}".strip())
 
 
@@ -180,6 +183,15 @@ def cdrge_get_work(ctx, kind: int) -> float:
     w = ctypes.c_double()
     _check(lib().cdrge_get_work(ctx, kind, ctypes.byref(w)), "cdrge_get_work")
     return w.value
+
+
+def cdrge_step_noalloc(cfg: cdrge_config, params, tokens, step: int, losses, stream=None):
+    _check(lib().cdrge_step_noalloc(ctypes.byref(cfg), _ptr(params), _ptr(tokens), step, _ptr(losses),
+                                    _stream_handle(stream)), "cdrge_step_noalloc")
+
+
+def cdrge_noalloc_max_workspace_bytes() -> int:
+    return int(lib().cdrge_noalloc_max_workspace_bytes())
 
 
 class Context:

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -636,6 +637,33 @@ cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   return CDRGE_OK;
 }
 
+// The library's own device scratch for cdrge_step_noalloc: the workspace of one configuration
+// whose plan fits in kScratchBytes. Each device holds its own copy from module load until the
+// process ends. In host code `scratch` names a host-side stand-in, never the device memory: host
+// code only ever uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Address of this device's scratch, looked up once per device with that device current.
+cdrge_status device_scratch(void** out) {
+  int dev = 0;
+  CDRGE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices) return CDRGE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    CDRGE_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) % kAlign) != 0) return CDRGE_ERR_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CDRGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -781,6 +809,33 @@ cdrge_status cdrge_get_work(cdrge_ctx* ctx, int kind, double* work) {
   if (!ctx || kind < 0 || kind > 3 || !work) return CDRGE_ERR_INVALID_ARG;
   *work = ctx->work[kind];
   return CDRGE_OK;
+}
+
+size_t cdrge_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+cdrge_status cdrge_step_noalloc(const cdrge_config* cfg, void* params, const int32_t* tokens,
+                                uint64_t step, float* losses, void* stream) {
+  if (!params || !tokens || !losses) return CDRGE_ERR_INVALID_ARG;
+  const cdrge_status st = cdrge_check_config(cfg);
+  if (st != CDRGE_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(params) % 16) != 0) return CDRGE_ERR_INVALID_ARG;
+  // a context on the stack, bound to the device's scratch instead of a caller workspace
+  cdrge_ctx ctx;
+  ctx.plan = make_plan(cfg);
+  if (ctx.plan.total > kScratchBytes) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "cdrge_step_noalloc: the configuration needs %zu workspace bytes, the static scratch holds %zu",
+                  ctx.plan.total, kScratchBytes);
+    return CDRGE_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  CDRGE_TRY(device_scratch(&ws));
+  ctx.params = params;
+  ctx.ws = static_cast<char*>(ws);
+  ctx.stream = static_cast<hipStream_t>(stream);
+  CDRGE_TRY(init_device(&ctx, cfg));  // clears the status words the previous call left
+  CDRGE_TRY(enqueue_probe_losses(&ctx, tokens, step, losses, nullptr));
+  return enqueue_update(&ctx, step, losses);
 }
 
 }  // extern "C"
