@@ -37,7 +37,11 @@ def test_record_contract(path):
     assert TOP_KEYS <= set(d), TOP_KEYS - set(d)
     assert d["n_gpus"] == 1 and d["higher_is_better"] is True and d["vs_baseline"] is None
     assert d["data"] == "synthetic" and d["scaling"] in ("weak", "strong")
-    assert d["config"]["workload"] == os.path.basename(path)[len("bench_"):-len(".json")]
+    name = os.path.basename(path)[len("bench_"):-len(".json")]
+    if "_seqlen" in name:  # the same workload at another sequence length
+        name, T = name.split("_seqlen")
+        assert d["config"]["seq_len"] == int(T)
+    assert d["config"]["workload"] == name
     # value is whole-step throughput: 2K * B * T perturbed-forward tokens per step over ms_per_step
     c = d["config"]
     tokens = 2 * c["n_probes"] * c["batch"] * c["seq_len"]

@@ -328,3 +328,23 @@ def test_probe_dominant_bf16(oracle, name):
     assert oracle.update(oc, ref_theta, 2, ref_l) == 0
     assert_theta_close(oracle, c, run.theta(), ref_theta, 2e-2)
     run.close()
+
+
+def test_long_sequence_charlm_widths(oracle):
+    # The char-LM widths (E = 128, H = 1024, two layers) over T = 200 steps: the forward streams
+    # through the same fixed-size state (h ping-pong per layer, c per tile) however long the
+    # sequence, and the losses and their probe differences still match the oracle.
+    c = b.make_config(2, 50, 128, 1024, 5, 200, 2, "bf16", 1e-4, 1e-4, 3103)
+    say("[gpu] long sequence, char-LM widths, T=200")
+    theta, tokens = _inputs(c, 14)
+    run = HipRun(c, theta, tokens)
+    losses, seq, st = run.probe_losses(0)
+    assert st == 0
+    seqs = [0, 2, 4]
+    ref_l, ref_seq = oracle.probe_losses(ocfg(c), theta, tokens, 0, seq_ids=seqs)
+    got = seq[:, seqs]
+    err = assert_losses_close(got, ref_seq, 2e-2, "seq_losses")
+    e = assert_diffs_close(got, ref_seq)
+    say(f"    seq-loss max rel err {err:.2e}; probe differences at {max(e):.3f} x the bar")
+    np.testing.assert_allclose(losses, seq.astype(np.float64).sum(1) / (c.batch * c.seq_len), rtol=1e-6)
+    run.close()
