@@ -6,7 +6,8 @@ cross-entropy losses (cdrge_probe_losses), then the seed-regenerating update (cd
 The default workload is the largest one that fits one GPU, the ~1.1B-parameter model: 4-layer
 LSTM, E = H = 5888, V = 50, bf16 weights with fp32 accumulation, batch 256, sequence length 10,
 K = 16 probe pairs evaluated in chunks of 8, eps = eta = 1e-4, Zipf(1.1) tokens. --workload
-selects the others (tiny, overfit, charlm, lstm270m).
+selects the others (tiny, overfit, charlm, lstm270m, and the transduction tasks copy, reverse and
+rollsum, which score only the output part of each sequence).
 
 Printed JSON line:
   value        perturbed-forward tokens per second over whole steps, 2K * B * T / step time
@@ -104,17 +105,21 @@ def cpu_worker(args) -> None:
     from oracle import Oracle
     from zero_order_recurrent_amd.inputs import PRESETS
     theta = np.load(os.path.join(args.cpu_worker, "theta.npy"), mmap_mode="r")
-    tokens = np.load(os.path.join(args.cpu_worker, "tokens.npy"))
-    p = PRESETS[args.workload].with_(seq_len=tokens.shape[1] - 1)
+    inputs = np.load(os.path.join(args.cpu_worker, "inputs.npy"))
+    targets = np.load(os.path.join(args.cpu_worker, "targets.npy"))
+    p = PRESETS[args.workload].with_(seq_len=inputs.shape[1])
     o = Oracle()
     seqs = [int(v) for v in args.worker_seqs.split(",")]
+    # everything is loaded: wait for the parent's start signal, so that all workers run together
+    print("ready", flush=True)
+    sys.stdin.readline()
     t0 = time.perf_counter()
-    o.probe_losses(_oracle_config(p), theta, tokens, 0, probe_ids=[args.worker_probe], seq_ids=seqs)
+    o.probe_losses_io(_oracle_config(p), theta, inputs, targets, 0, probe_ids=[args.worker_probe], seq_ids=seqs)
     dt = time.perf_counter() - t0
     print(json.dumps({"seconds": dt, "tokens": 2 * len(seqs) * p.seq_len}), flush=True)
 
 
-def cpu_baseline(preset, theta, tokens, budget_s: float) -> dict:
+def cpu_baseline(preset, theta, inputs, targets, budget_s: float) -> dict:
     """The oracle (plain single-threaded C++) on the host's cores, on a bounded sample of the
     workload: one probe pair, both signs, over full sequences, at full model shape, including the
     perturbed parameter copies the oracle builds for each sign.
@@ -134,7 +139,7 @@ def cpu_baseline(preset, theta, tokens, budget_s: float) -> dict:
 
     def timed(probe, seqs):
         t0 = time.perf_counter()
-        o.probe_losses(oc, theta, tokens, 0, probe_ids=[probe], seq_ids=list(seqs))
+        o.probe_losses_io(oc, theta, inputs, targets, 0, probe_ids=[probe], seq_ids=list(seqs))
         return time.perf_counter() - t0
 
     t_copies = timed(0, [])                      # two perturbed copies, no forward
@@ -174,9 +179,9 @@ def cpu_baseline(preset, theta, tokens, budget_s: float) -> dict:
         tmp = tempfile.mkdtemp(prefix="cdrge_cpu_")
         try:
             np.save(os.path.join(tmp, "theta.npy"), theta)
-            np.save(os.path.join(tmp, "tokens.npy"), tokens)
+            np.save(os.path.join(tmp, "inputs.npy"), inputs)
+            np.save(os.path.join(tmp, "targets.npy"), targets)
             procs = []
-            t0 = time.perf_counter()
             for w in range(workers):
                 probe = w % preset.n_probes
                 first = (w // preset.n_probes) * n_each
@@ -184,7 +189,14 @@ def cpu_baseline(preset, theta, tokens, budget_s: float) -> dict:
                 procs.append(subprocess.Popen(
                     [sys.executable, os.path.abspath(__file__), "--workload", preset.name, "--cpu-worker", tmp,
                      "--worker-probe", str(probe), "--worker-seqs", seqs],
-                    stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+                    stdin=subprocess.PIPE, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+            for pr in procs:  # every worker has its inputs loaded
+                if pr.stdout.readline().strip() != "ready":
+                    raise RuntimeError(f"oracle worker failed to start: {pr.stderr.read()[-400:]}")
+            t0 = time.perf_counter()
+            for pr in procs:
+                pr.stdin.write("go\n")
+                pr.stdin.flush()
             outs = []
             for pr in procs:
                 out, err = pr.communicate()
@@ -193,7 +205,7 @@ def cpu_baseline(preset, theta, tokens, budget_s: float) -> dict:
                 outs.append(json.loads(out.strip().splitlines()[-1]))
             wall = time.perf_counter() - t0
         finally:
-            for name in ("theta.npy", "tokens.npy"):
+            for name in ("theta.npy", "inputs.npy", "targets.npy"):
                 try:
                     os.remove(os.path.join(tmp, name))
                 except OSError:
@@ -271,16 +283,21 @@ def main():
               "is described, not built). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    from zero_order_recurrent_amd.inputs import PRESETS, make_theta, make_tokens
+    from zero_order_recurrent_amd.inputs import PRESETS, make_io, make_theta, make_tokens
 
     p = PRESETS[args.workload]
     if args.seq_len > 0:
+        if p.task != "lm":
+            print("--seq-len applies to the language-model workloads", file=sys.stderr)
+            sys.exit(2)
         p = p.with_(seq_len=args.seq_len)
     theta_host = make_theta(p, _param_count(p))
-    tokens_host = make_tokens(p)
+    lm = p.task == "lm"
+    tokens_host = make_tokens(p) if lm else None
+    inputs_host, targets_host = make_io(p)
     # The CPU legs run first, before this process touches the GPU: the all-cores leg starts
     # child processes, and the GPU then sits idle rather than sharing the host with them.
-    cpu = None if args.no_cpu_baseline else cpu_baseline(p, theta_host, tokens_host, args.cpu_budget)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(p, theta_host, inputs_host, targets_host, args.cpu_budget)
 
     import torch
     from zero_order_recurrent_amd import binding as b
@@ -288,15 +305,24 @@ def main():
     cfg = b.config_from_preset(p)
     d = b.cdrge_param_count(cfg)
     assert d == theta_host.size
-    if p.dtype == "bf16":
+    bf16 = p.dtype != "f32"
+    if bf16:
         params = torch.from_numpy(theta_host.view(np.int16).copy()).cuda()
     else:
         params = torch.from_numpy(theta_host.copy()).cuda()
-    tokens = torch.from_numpy(tokens_host).cuda()
     ctx = b.Context(cfg, params)
+    if lm:
+        tokens = torch.from_numpy(tokens_host).cuda()
+        run_step = lambda s: ctx.step(tokens, s)  # noqa: E731
+        run_fwd = lambda s: ctx.probe_losses(tokens, s)  # noqa: E731
+    else:
+        inputs = torch.from_numpy(inputs_host).cuda()
+        targets = torch.from_numpy(targets_host).cuda()
+        run_step = lambda s: ctx.step_io(inputs, targets, s)  # noqa: E731
+        run_fwd = lambda s: ctx.probe_losses_io(inputs, targets, s)  # noqa: E731
 
     for s in range(args.warmup):
-        ctx.step(tokens, s)
+        run_step(s)
     st = ctx.sync_status()
     if st != 0:
         print(f"warmup steps ended with {b.STATUS[st]}", file=sys.stderr)
@@ -307,7 +333,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        ctx.step(tokens, args.warmup + s)
+        run_step(args.warmup + s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     b.cdrge_set_timing(ctx.ctx, False)
@@ -324,7 +350,7 @@ def main():
     t1 = time.perf_counter()
     n_fwd = max(1, args.steps // 2)
     for s in range(n_fwd):
-        ctx.probe_losses(tokens, 1000 + s)
+        run_fwd(1000 + s)
     torch.cuda.synchronize()
     fwd_s = (time.perf_counter() - t1) / n_fwd
 
@@ -334,9 +360,9 @@ def main():
     gate_flops_per_launch = work[0] / max(gate_n, 1)
     gate_mean_s = gate_ms / 1e3 / max(gate_n, 1)
     achieved = gate_flops_per_launch / gate_mean_s / 1e12 if gate_n else 0.0
-    peak = PEAK["bf16_mfma_tflops"] if p.dtype == "bf16" else PEAK["fp32_tflops"]
-    traffic = traffic_from_profiles("gates_bf16" if p.dtype == "bf16" else "lstm_f32", args.workload)
-    upd_traffic = traffic_from_profiles("update_bf16" if p.dtype == "bf16" else "update_f32", args.workload)
+    peak = PEAK["bf16_mfma_tflops"] if bf16 else PEAK["fp32_tflops"]
+    traffic = traffic_from_profiles("gates_bf16" if bf16 else "lstm_f32", args.workload)
+    upd_traffic = traffic_from_profiles("update_bf16" if bf16 else "update_f32", args.workload)
     upd_ms, upd_n = timing[2]
     upd_gbs = work[2] / (upd_ms / 1e3) / 1e9 if upd_n else 0.0
     ce_ms, ce_n = timing[1]
@@ -352,22 +378,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if p.dtype == "bf16" else "f32",
+        "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": p.name, "n_layers": p.n_layers, "embed": p.embed, "hidden": p.hidden,
                    "vocab": p.vocab, "batch": p.batch, "seq_len": p.seq_len, "n_probes": p.n_probes,
                    "probes_per_chunk": p.probes_per_chunk, "eps": p.eps, "lr": p.lr, "params": d,
-                   "tokens": p.tokens},
+                   **({"perturbation": "exact (W x +- eps' P x, eps' = bf16(eps); twice the matrix-core work)"}
+                      if p.dtype == "bf16x" else {}),
+                   **({"tokens": p.tokens} if lm else
+                      {"task": p.task, "source_lengths": [p.min_len, p.max_len],
+                       "scored_positions": int((targets_host >= 0).sum())})},
         "cdrge_steps_per_sec": 1.0 / step_s,
         "ms_per_timestep": step_s * 1e3 / p.seq_len,
         "workspace_bytes": b.cdrge_workspace_bytes(cfg),
         "forward_only_tokens_per_sec": tokens_per_step / fwd_s,
-        "roofline": {"bound": "mfma" if p.dtype == "bf16" else "alu", "kernel": "k_lstm_gates_bf16"
-                     if p.dtype == "bf16" else "k_lstm_f32",
+        "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": "k_lstm_gates_bf16"
+                     if bf16 else "k_lstm_f32",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "launches": gate_n, "mean_launch_ms": gate_mean_s * 1e3,
                      "flops_per_launch": gate_flops_per_launch},
-        "update_roofline": {"bound": "hbm", "kernel": "k_update_perm" if p.dtype == "bf16" and p.n_probes <= 64
+        "update_roofline": {"bound": "hbm", "kernel": "k_update_perm" if bf16 and p.n_probes <= 64
                             else "k_update_lut", "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
                             "frac": upd_gbs / PEAK["hbm_gbs"], "traffic": upd_traffic, "launches": upd_n,
                             "total_ms_per_step": upd_ms / args.steps,

@@ -32,7 +32,7 @@
  * stored as bf16; a perturbed weight is bf16(float(w) +- eps) rounded to nearest even; matrix
  * products take bf16 operands (activations are rounded to bf16 where they enter a product) and
  * accumulate in float32; cell state, gates, logits and losses are float32; the update adds in
- * float32 and rounds to bf16.
+ * float32 and rounds to bf16. dtype BF16_EXACT: as BF16, but the probe is added exactly (below).
  *
  * Conventions shared by every call:
  *   - Pointers named as device pointers must be device memory of the GPU that was current at
@@ -65,7 +65,16 @@ typedef enum {
   CDRGE_ERR_NONFINITE = 5    /* a probe loss was NaN or infinite; the update left theta as is */
 } cdrge_status;
 
-typedef enum { CDRGE_F32 = 0, CDRGE_BF16 = 1 } cdrge_dtype;
+/* CDRGE_BF16_EXACT: bf16 parameters with the probe added exactly. A radius eps below the bf16
+ * spacing of a weight (eps = 1e-4 against |w| around 2^-6 .. 2^-5) is swallowed when the perturbed
+ * weight is rounded back to bf16; here every matrix product takes the stored weights W and the
+ * exact bf16 operand eps' P, eps' = bf16(eps), into the same float32 accumulator:
+ * (W +- eps' P) x = W x +- eps' (P x), twice the matrix-core work of CDRGE_BF16. Biases get
+ * +- eps' p in float32; the perturbed embedding rows are rounded to bf16 (they are the first
+ * product's activations); activations are rounded as for CDRGE_BF16. The update uses
+ * eta / (2 K eps'), the radius actually applied. (alex-wiki source note, "Method": weights
+ * perturbed by eps u_i; the pages fix no precision.) */
+typedef enum { CDRGE_F32 = 0, CDRGE_BF16 = 1, CDRGE_BF16_EXACT = 2 } cdrge_dtype;
 
 typedef struct {
   uint32_t abi_version;     /* must be CDRGE_ABI_VERSION */
@@ -93,7 +102,7 @@ int64_t cdrge_param_count(const cdrge_config* cfg);
  *   sums for up to 2 probe pairs x 8 sequences - fits in 128 KB (about
  *   4 * m * (2 L H + 5 max(E, H) + 4 H) bytes for m = 2 * pairs * sequences per workgroup, plus
  *   8 L H bytes of biases);
- *   BF16 when E % 32 == 0, H % 32 == 0, V <= 64, and one probe chunk's activations stay within
+ *   BF16 and BF16_EXACT when E % 32 == 0, H % 32 == 0, V <= 64, and one probe chunk's activations stay within
  *   32-bit element offsets: (2 * probes_per_chunk * B + 256) * max(E, H) < 2^31 and
  *   4 H max(E, H) < 2^31. */
 cdrge_status cdrge_check_config(const cdrge_config* cfg);
@@ -128,6 +137,23 @@ cdrge_status cdrge_update(cdrge_ctx* ctx, uint64_t step, const float* losses);
 
 /* cdrge_probe_losses followed by cdrge_update on the same stream. */
 cdrge_status cdrge_step(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step, float* losses);
+
+/* Transduction form of cdrge_probe_losses, for the synthetic sequence-to-sequence tasks the pages
+ * also train on (alex-wiki source note, "Evidence And Limits": copy, reverse and rolling sum,
+ * where only the output part of a sequence is scored).
+ *   inputs: device int32 [B][T], every entry in [0, V): the token fed at (b, t).
+ *   targets: device int32 [B][T]: the token to predict at (b, t), in [0, V), or below zero for a
+ *     position that is not scored.
+ * The loss of a perturbed model is the mean cross-entropy over the scored positions of the batch
+ * (NaN when none is scored or an entry is out of range); seq_losses, when not NULL, gets the
+ * per-sequence sums over the scored positions. cdrge_probe_losses(tokens) is this call with
+ * inputs = tokens[:, 0:T] and targets = tokens[:, 1:T+1]. */
+cdrge_status cdrge_probe_losses_io(cdrge_ctx* ctx, const int32_t* inputs, const int32_t* targets,
+                                   uint64_t step, float* losses, float* seq_losses);
+
+/* cdrge_probe_losses_io followed by cdrge_update on the same stream. */
+cdrge_status cdrge_step_io(cdrge_ctx* ctx, const int32_t* inputs, const int32_t* targets, uint64_t step,
+                           float* losses);
 
 /* Waits for the context's stream and reports deferred errors (non-finite losses, device
  * faults). Clears the non-finite flag. */

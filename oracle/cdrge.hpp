@@ -21,6 +21,14 @@
 //     difference of the float losses, the sum over probes and the step are evaluated in double
 //     and the result is rounded once to the storage precision.
 //   * Any non-finite loss leaves theta unchanged and reports an error.
+//   * Exact-perturbation bf16 (storage BF16_EXACTP): bf16 parameters, but the probe is added
+//     without rounding the perturbed weight back to bf16, so that radii below the bf16 spacing of
+//     a weight still reach the loss: a matrix or bias element becomes w + s * eps' exactly, with
+//     eps' = bf16(eps), the radius a bf16 operand can carry (the alex-wiki "Method" section
+//     perturbs the weights by eps u_i; the pages fix no precision). The embedding rows are the
+//     first product's activations and are rounded to bf16 after the perturbation like every
+//     activation. The update's coefficient is eta / (2 K eps'): the central difference of the
+//     losses divided by twice the radius actually applied.
 #pragma once
 #include <cmath>
 #include <cstdint>
@@ -32,13 +40,21 @@
 
 namespace oracle {
 
-enum class Storage { F32 = 0, BF16 = 1, F64 = 2 };
+enum class Storage { F32 = 0, BF16 = 1, F64 = 2, BF16_EXACTP = 3 };
+
+inline bool bf16_weights(Storage s) { return s == Storage::BF16 || s == Storage::BF16_EXACTP; }
+
+// The probe radius applied: eps, or bf16(eps) for the exact-perturbation bf16 model.
+inline double probe_radius(Storage s, float eps) {
+  return s == Storage::BF16_EXACTP ? static_cast<double>(bf16_to_f32(f32_to_bf16(eps))) : static_cast<double>(eps);
+}
 
 // Reads a stored parameter as a double.
 inline double load_param(const void* theta, Storage s, int64_t j) {
   switch (s) {
     case Storage::F32: return static_cast<const float*>(theta)[j];
-    case Storage::BF16: return bf16_to_f32(static_cast<const uint16_t*>(theta)[j]);
+    case Storage::BF16:
+    case Storage::BF16_EXACTP: return bf16_to_f32(static_cast<const uint16_t*>(theta)[j]);
     default: return static_cast<const double*>(theta)[j];
   }
 }
@@ -47,14 +63,21 @@ inline double load_param(const void* theta, Storage s, int64_t j) {
 inline void store_param(void* theta, Storage s, int64_t j, double x) {
   switch (s) {
     case Storage::F32: static_cast<float*>(theta)[j] = static_cast<float>(x); break;
-    case Storage::BF16: static_cast<uint16_t*>(theta)[j] = f64_to_bf16(x); break;
+    case Storage::BF16:
+    case Storage::BF16_EXACTP: static_cast<uint16_t*>(theta)[j] = f64_to_bf16(x); break;
     default: static_cast<double*>(theta)[j] = x; break;
   }
 }
 
-// The perturbed weight w + sigma * eps * p in the storage precision (see the header comment).
-inline double perturbed_param(double w, Storage s, int signed_unit, float eps) {
+// The perturbed weight w + sigma * eps * p in the storage precision (see the header comment);
+// `activation` marks an element that enters a product as an activation (the embedding rows).
+inline double perturbed_param(double w, Storage s, int signed_unit, float eps, bool activation = false) {
   switch (s) {
+    case Storage::BF16_EXACTP: {
+      const double r = probe_radius(s, eps);
+      if (activation) return round_to_bf16(static_cast<double>(static_cast<float>(w) + static_cast<float>(signed_unit * r)));
+      return w + signed_unit * r;
+    }
     case Storage::F32: {
       const float sum = static_cast<float>(w) + static_cast<float>(signed_unit) * eps;
       return sum;
@@ -139,7 +162,7 @@ void perturbed_copy(const std::vector<TensorInfo>& lay, const void* theta, Stora
       for (int64_t c = 0; c < t.cols; ++c) {
         const int64_t j = t.offset + r * t.cols + c;
         const int p = sign(seed, t.id, static_cast<uint32_t>(r), static_cast<uint32_t>(c));
-        out[j] = static_cast<P>(perturbed_param(load_param(theta, s, j), s, sigma * p, eps));
+        out[j] = static_cast<P>(perturbed_param(load_param(theta, s, j), s, sigma * p, eps, t.id == 0));
       }
 }
 
@@ -181,7 +204,7 @@ int cdrge_update(const std::vector<TensorInfo>& lay, void* theta, Storage s, uin
     dif[i] = losses[2 * i] - losses[2 * i + 1];
     seeds[i] = probe_seed(base_seed, step, static_cast<uint32_t>(i));
   }
-  const double coef = update_coef(K, eps, lr);
+  const double coef = update_coef(K, static_cast<float>(probe_radius(s, eps)), lr);
   LayoutIndexer index(lay);
   std::vector<SignReader> sign(K);  // one per probe, so consecutive elements reuse their block
   const int64_t n = elems ? n_elems : layout_size(lay);

@@ -40,7 +40,7 @@ class _Cfg(ctypes.Structure):
                 ("lr", ctypes.c_float), ("base_seed", ctypes.c_uint64)]
 
 
-STORAGE = {"f32": 0, "bf16": 1, "f64": 2}
+STORAGE = {"f32": 0, "bf16": 1, "f64": 2, "bf16x": 3}
 
 
 @dataclass
@@ -52,7 +52,7 @@ class OracleConfig:
     batch: int
     seq_len: int
     n_probes: int
-    storage: str  # "f32", "bf16" (uint16 bit patterns) or "f64" (exact)
+    storage: str  # "f32", "bf16" (uint16 bit patterns), "f64" (exact) or "bf16x" (bf16, probe added exactly)
     eps: float
     lr: float
     base_seed: int

@@ -16,7 +16,7 @@ using namespace oracle;
 extern "C" {
 
 // Model and probe configuration. storage: 0 = fp32, 1 = bf16 (as uint16 bit patterns),
-// 2 = exact (double).
+// 2 = exact (double), 3 = bf16 parameters with the probe added exactly (cdrge.hpp).
 struct oracle_cfg {
   int32_t n_layers, vocab, embed, hidden, batch, seq_len, n_probes, storage;
   float eps, lr;
@@ -120,7 +120,7 @@ static void probe_losses_view(const oracle_cfg* c, const void* theta, const Toke
   const ModelShape m = shape_of(c);
   const auto lay = lstm_layout(m);
   const Storage s = static_cast<Storage>(c->storage);
-  const bool round_act = (s == Storage::BF16);
+  const bool round_act = bf16_weights(s);
   const double scored = static_cast<double>(scored_positions(tv, m.T, seq_ids, n_seq));
   std::vector<double> seq(n_seq);
   int side_index = 0;
@@ -136,7 +136,7 @@ static void probe_losses_view(const oracle_cfg* c, const void* theta, const Toke
     return total / scored;
   };
   std::vector<double> out(2 * int64_t(n_ids));
-  if (s == Storage::F64) {
+  if (s == Storage::F64 || s == Storage::BF16_EXACTP) {
     probe_losses_generic<double>(lay, theta, s, c->base_seed, step, probe_ids, n_ids, c->eps, loss,
                                  out.data());
   } else {

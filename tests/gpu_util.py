@@ -9,7 +9,8 @@ import numpy as np
 from oracle import OracleConfig
 from zero_order_recurrent_amd import binding as b
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "bf16x": 2e-2}
+NAMES = {b.CDRGE_F32: "f32", b.CDRGE_BF16: "bf16", b.CDRGE_BF16_EXACT: "bf16x"}
 
 
 def say(msg: str):
@@ -19,11 +20,11 @@ def say(msg: str):
 
 def ocfg(c: b.cdrge_config) -> OracleConfig:
     return OracleConfig(c.n_layers, c.vocab, c.embed, c.hidden, c.batch, c.seq_len, c.n_probes,
-                        "bf16" if c.dtype == b.CDRGE_BF16 else "f32", c.eps, c.lr, c.base_seed)
+                        NAMES[c.dtype], c.eps, c.lr, c.base_seed)
 
 
 def dtype_name(c: b.cdrge_config) -> str:
-    return "bf16" if c.dtype == b.CDRGE_BF16 else "f32"
+    return NAMES[c.dtype]
 
 
 def to_device_params(theta: np.ndarray):

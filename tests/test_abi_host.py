@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 def _ocfg(c):
     return OracleConfig(c.n_layers, c.vocab, c.embed, c.hidden, c.batch, c.seq_len, c.n_probes,
-                        "bf16" if c.dtype == b.CDRGE_BF16 else "f32", c.eps, c.lr, c.base_seed)
+                        {0: "f32", 1: "bf16", 2: "bf16x"}[c.dtype], c.eps, c.lr, c.base_seed)
 
 
 def test_param_count_matches_oracle(lib, oracle):

@@ -43,7 +43,7 @@ def _check(oracle, name, probes, seqs):
     rows = [2 * i + s for i in probes for s in (0, 1)]
     err = assert_losses_close(seq[np.ix_(rows, seqs)], ref_seq, tol, "seq_losses")
     say(f"    seq-loss max rel err {err:.2e}")
-    if p.dtype == "bf16":
+    if p.dtype != "f32":
         e = assert_diffs_close(seq[np.ix_(rows, seqs)], ref_seq)
         say(f"    probe differences at {max(e):.3f} x the bar")
     if len(seqs) == c.batch:
@@ -127,3 +127,8 @@ def test_full_layout_signs(oracle, name, probes):
         np.testing.assert_array_equal(vals, -coef * sgn.astype(np.float32))
     say(f"    {len(elems)} sampled elements per probe bit-exact")
     ctx.close()
+
+
+def test_full_charlm_exact_perturbation(oracle):
+    # the char-LM workload in the exact-perturbation bf16 dtype (same theta and tokens as charlm)
+    _check(oracle, "charlm_x", probes=[0, 63], seqs=[0, 1, 511, 1023])

@@ -45,7 +45,7 @@ def _inputs(c, seed):
     d = b.cdrge_param_count(c)
     bound = 1.0 / np.sqrt(c.hidden)
     theta = rng.uniform(-bound, bound, d).astype(np.float32)
-    if c.dtype == b.CDRGE_BF16:
+    if c.dtype != b.CDRGE_F32:
         theta = to_bf16_bits(theta)
     tokens = rng.integers(0, c.vocab, size=(c.batch, c.seq_len + 1)).astype(np.int32)
     return theta, tokens
@@ -64,7 +64,7 @@ def test_small_step_parity(oracle, name):
     ref_l, ref_seq = oracle.probe_losses(oc, theta, tokens, 2)
     assert_losses_close(losses, ref_l, tol)
     assert_losses_close(seq, ref_seq, tol, "seq_losses")
-    if c.dtype == b.CDRGE_BF16:
+    if c.dtype != b.CDRGE_F32:
         e = assert_diffs_close(seq, ref_seq)
         assert_diffs_close(losses[:, None], ref_l[:, None], "per-probe d_i")
         say(f"    probe differences at {max(e):.3f} x the bar")
@@ -347,4 +347,39 @@ def test_long_sequence_charlm_widths(oracle):
     e = assert_diffs_close(got, ref_seq)
     say(f"    seq-loss max rel err {err:.2e}; probe differences at {max(e):.3f} x the bar")
     np.testing.assert_allclose(losses, seq.astype(np.float64).sum(1) / (c.batch * c.seq_len), rtol=1e-6)
+    run.close()
+
+
+# The exact-perturbation bf16 dtype: bf16 parameters, (W +- eps' P) x = W x +- eps' P x with the
+# probe never rounded into the weight. Shapes as the bf16 cases: ragged batch, several row tiles,
+# chunks of unequal size, the split logits reduction, a probe-dominant eps and eps = 1e-4 where
+# the plain bf16 model quantises the probe.
+EXACT = {
+    "x_ragged": b.make_config(2, 50, 64, 128, 160, 3, 3, "bf16x", 1e-4, 1e-4, 701, probes_per_chunk=2),
+    "x_h256": b.make_config(2, 50, 96, 256, 300, 4, 4, "bf16x", 2.0 ** -7, 2.0 ** -7, 702),
+    "x_ce_split": b.make_config(1, 50, 32, 416, 40, 3, 2, "bf16x", 1e-3, 1e-3, 703),
+    "x_min": b.make_config(1, 2, 32, 32, 1, 1, 1, "bf16x", 1e-2, 1e-2, 704),
+    "x_e2m3": b.make_config(2, 50, 64, 128, 160, 3, 3, "bf16x", 2.0 ** -3, 2.0 ** -3, 705),
+}
+
+
+@pytest.mark.parametrize("name", list(EXACT))
+def test_exact_perturbation_bf16(oracle, name):
+    c = EXACT[name]
+    say(f"[gpu] exact-perturbation bf16 {name}")
+    theta, tokens = _inputs(c, 15)
+    run = HipRun(c, theta, tokens)
+    losses, seq, st = run.probe_losses(step=1)
+    assert st == 0
+    oc = ocfg(c)
+    ref_l, ref_seq = oracle.probe_losses(oc, theta, tokens, 1)
+    assert_losses_close(losses, ref_l, 2e-2)
+    assert_losses_close(seq, ref_seq, 2e-2, "seq_losses")
+    e = assert_diffs_close(seq, ref_seq)
+    assert_diffs_close(losses[:, None], ref_l[:, None], "per-probe d_i")
+    say(f"    probe differences at {max(e):.3f} x the bar")
+    assert run.update(1) == 0
+    ref_theta = theta.copy()
+    assert oracle.update(oc, ref_theta, 1, ref_l) == 0
+    assert_theta_close(oracle, c, run.theta(), ref_theta, 2e-2)
     run.close()

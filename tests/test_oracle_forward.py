@@ -272,3 +272,58 @@ def test_lm_form_is_the_io_form_with_shifted_targets(oracle):
     b = oracle.probe_losses_io(cfg, w16, tokens[:, :-1].copy(), tokens[:, 1:].copy(), 1)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_exact_perturbation_bf16_matches_torch(oracle):
+    """The exact-perturbation bf16 model (storage 'bf16x'): bf16 parameters, the probe added without
+    rounding back to bf16 at radius eps' = bf16(eps): w + s eps' p for every matrix and bias
+    element (formed here in float64, where it is exact), bf16(fl32(w + s eps' p)) for the
+    embedding rows (activations of the first product). Then the bf16 torch model above
+    (activations rounded where they enter a product). eps = 3e-3 sits below the bf16 spacing of
+    most of these weights, so the plain bf16 model swallows most of the probe and this one does
+    not."""
+    shape = SHAPES[1]
+    cfg = OracleConfig(n_probes=2, storage="bf16x", eps=3e-3, lr=3e-3, base_seed=81, **shape)
+    d = oracle.param_count(cfg)
+    rng = np.random.default_rng(28)
+    w16 = _bf16_bits(rng.uniform(-0.6, 0.6, d))
+    tokens = rng.integers(0, cfg.vocab, size=(cfg.batch, cfg.seq_len + 1)).astype(np.int32)
+    step = 2
+    _, seq = oracle.probe_losses(cfg, w16, tokens, step)
+    r = float(torch.tensor(cfg.eps, dtype=torch.float32).to(torch.bfloat16).to(torch.float64))
+    assert r != cfg.eps
+    w64 = _bits_to_f64(w16)
+    lay = {tid: (off, rows, cols) for tid, off, rows, cols in oracle.layout(cfg)}
+    off0, rows0, cols0 = lay[0]
+    emb = slice(off0, off0 + rows0 * cols0)
+    plain = OracleConfig(n_probes=2, storage="bf16", eps=3e-3, lr=3e-3, base_seed=81, **shape)
+    _, seq_plain = oracle.probe_losses(plain, w16, tokens, step)
+    for i in range(cfg.n_probes):
+        p = oracle.probe_vector(cfg, oracle.probe_seed(cfg.base_seed, step, i)).astype(np.float64)
+        for side, sgn in enumerate((1.0, -1.0)):
+            pert = w64 + sgn * r * p
+            e32 = torch.from_numpy(w64[emb].astype(np.float32)) + torch.tensor(sgn * r, dtype=torch.float32) * \
+                torch.from_numpy(p[emb].astype(np.float32))
+            pert[emb] = e32.to(torch.bfloat16).to(torch.float64).numpy()
+            ref = torch_bf16_seq_losses(oracle, cfg, pert, tokens)
+            np.testing.assert_allclose(seq[2 * i + side], ref, rtol=1e-12, atol=0)
+        # the probe differences of the two definitions differ well beyond rounding
+        dx = seq[2 * i] - seq[2 * i + 1]
+        dp = seq_plain[2 * i] - seq_plain[2 * i + 1]
+        assert np.max(np.abs(dx - dp)) > 0.05 * np.max(np.abs(dx))
+
+
+def test_exact_perturbation_update_uses_the_applied_radius(oracle):
+    # theta = 0, d = e_0: theta' = bf16(-eta / (2 K eps') p_0), eps' = bf16(eps)
+    shape = SHAPES[0]
+    cfg = OracleConfig(n_probes=4, storage="bf16x", eps=1e-4, lr=1e-4, base_seed=82, **shape)
+    d = oracle.param_count(cfg)
+    theta = np.zeros(d, np.uint16)
+    losses = np.zeros(8, np.float32)
+    losses[0] = 1.0
+    assert oracle.update(cfg, theta, 0, losses) == 0
+    r = float(torch.tensor(1e-4, dtype=torch.float32).to(torch.bfloat16).to(torch.float64))
+    coef = np.float32(float(np.float32(1e-4)) / (2.0 * 4 * float(np.float32(r))))  # double, rounded once
+    p = oracle.probe_vector(cfg, oracle.probe_seed(cfg.base_seed, 0, 0)).astype(np.float32)
+    want = torch.from_numpy(-coef * p).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(theta, want)

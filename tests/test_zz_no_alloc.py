@@ -27,7 +27,7 @@ def _inputs(c, seed):
     d = b.cdrge_param_count(c)
     bound = 1.0 / np.sqrt(c.hidden)
     theta = rng.uniform(-bound, bound, d).astype(np.float32)
-    if c.dtype == b.CDRGE_BF16:
+    if c.dtype != b.CDRGE_F32:
         theta = to_bf16_bits(theta)
     tokens = rng.integers(0, c.vocab, size=(c.batch, c.seq_len + 1)).astype(np.int32)
     return theta, tokens

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcdrge.so")
 
 CDRGE_ABI_VERSION = 1
-CDRGE_F32, CDRGE_BF16 = 0, 1
+CDRGE_F32, CDRGE_BF16, CDRGE_BF16_EXACT = 0, 1, 2
 STATUS = {0: "CDRGE_OK", 1: "CDRGE_ERR_INVALID_ARG", 2: "CDRGE_ERR_UNSUPPORTED", 3: "CDRGE_ERR_WORKSPACE",
           4: "CDRGE_ERR_DEVICE", 5: "CDRGE_ERR_NONFINITE"}
 KIND_GATES, KIND_CE, KIND_UPDATE, KIND_PREP = 0, 1, 2, 3
@@ -36,7 +36,7 @@ class cdrge_config(ctypes.Structure):
 
 def make_config(n_layers, vocab, embed, hidden, batch, seq_len, n_probes, dtype, eps, lr, base_seed,
                 probes_per_chunk=0) -> cdrge_config:
-    dt = {"f32": CDRGE_F32, "bf16": CDRGE_BF16}.get(dtype, dtype)
+    dt = {"f32": CDRGE_F32, "bf16": CDRGE_BF16, "bf16x": CDRGE_BF16_EXACT}.get(dtype, dtype)
     return cdrge_config(CDRGE_ABI_VERSION, n_layers, vocab, embed, hidden, batch, seq_len, n_probes,
                         probes_per_chunk, dt, eps, lr, base_seed)
 
@@ -67,6 +67,10 @@ EXPORTS = {
     "cdrge_get_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int]),
     "cdrge_get_work": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
+    "cdrge_probe_losses_io": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
+    "cdrge_step_io": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                     ctypes.c_void_p]),
     "cdrge_step_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                           ctypes.c_void_p, ctypes.c_void_p]),
     "cdrge_noalloc_max_workspace_bytes": (ctypes.c_size_t, []),
@@ -152,6 +156,15 @@ def cdrge_step(ctx, tokens, step: int, losses):
     _check(lib().cdrge_step(ctx, _ptr(tokens), step, _ptr(losses)), "cdrge_step")
 
 
+def cdrge_probe_losses_io(ctx, inputs, targets, step: int, losses, seq_losses=None):
+    _check(lib().cdrge_probe_losses_io(ctx, _ptr(inputs), _ptr(targets), step, _ptr(losses), _ptr(seq_losses)),
+           "cdrge_probe_losses_io")
+
+
+def cdrge_step_io(ctx, inputs, targets, step: int, losses):
+    _check(lib().cdrge_step_io(ctx, _ptr(inputs), _ptr(targets), step, _ptr(losses)), "cdrge_step_io")
+
+
 def cdrge_sync_status(ctx) -> int:
     return int(lib().cdrge_sync_status(ctx))
 
@@ -222,6 +235,14 @@ class Context:
 
     def step(self, tokens, step: int):
         cdrge_step(self.ctx, tokens, step, self.losses)
+        return self.losses
+
+    def probe_losses_io(self, inputs, targets, step: int, seq_losses=None):
+        cdrge_probe_losses_io(self.ctx, inputs, targets, step, self.losses, seq_losses)
+        return self.losses
+
+    def step_io(self, inputs, targets, step: int):
+        cdrge_step_io(self.ctx, inputs, targets, step, self.losses)
         return self.losses
 
     def sync_status(self) -> int:

@@ -30,6 +30,22 @@ constexpr int64_t kMaxF32LdsBytes = 128 * 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Nearest bf16 to x (ties to even), as a float. x is finite.
+float round_bf16_host(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+  float r;
+  std::memcpy(&r, &u, 4);
+  return r;
+}
+
+// The probe radius the kernels apply: eps, or bf16(eps) for the exact-perturbation bf16 model,
+// whose perturbation enters the matrix products as the bf16 operand eps' P.
+float probe_radius(const cdrge_config& c) {
+  return c.dtype == CDRGE_BF16_EXACT ? round_bf16_host(c.eps) : c.eps;
+}
+
 // Text of the last device-side failure seen by this thread (for cdrge_last_error_detail).
 thread_local char g_last_error[256] = "";
 
@@ -70,7 +86,7 @@ bool basic_valid(const cdrge_config* c) {
   if (c->n_layers < 1 || c->vocab < 2 || c->embed < 1 || c->hidden < 1 || c->batch < 1 ||
       c->seq_len < 1 || c->n_probes < 1 || c->probes_per_chunk < 0)
     return false;
-  if (c->dtype != CDRGE_F32 && c->dtype != CDRGE_BF16) return false;
+  if (c->dtype != CDRGE_F32 && c->dtype != CDRGE_BF16 && c->dtype != CDRGE_BF16_EXACT) return false;
   if (!std::isfinite(c->eps) || !(c->eps > 0.f) || !std::isfinite(c->lr) || c->lr < 0.f) return false;
   return true;
 }
@@ -161,7 +177,7 @@ Plan make_plan(const cdrge_config* c) {
   p.off_emb_m = p.off_bias_m = p.off_bout_m = p.off_x0 = p.off_h = p.off_c = 0;
   p.ncols_pad = ncols + kTileCols;
   p.n_tiles = int64_t(p.H / kUnitsPerTile) * ((p.B + kTileCols - 1) / kTileCols) * p.P;
-  if (c->dtype == CDRGE_BF16) {
+  if (c->dtype != CDRGE_F32) {
     for (const TensorDesc& t : p.tensors) {
       if (t.id != static_cast<uint32_t>(1 + 3 * p.L)) continue;  // W_out: candidates for the logits kernel
       p.off_wp[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
@@ -267,23 +283,38 @@ cdrge_status timed(cdrge_ctx* ctx, int kind, double work, F&& launch) {
     if (_s != CDRGE_OK) return _s;        \
   } while (0)
 
-cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step,
-                                  float* losses, float* seq_losses) {
+// Where the kernels read the input and the target of (sequence b, step t): in[b * in_stride + t]
+// and tg[b * tg_stride + t]. The language-model form reads both from tokens [B][T+1] (target =
+// next token, all scored); the transduction form takes [B][T] arrays and allows unscored targets.
+struct TokenRefs {
+  const int32_t* in;
+  int in_stride;
+  const int32_t* tg;
+  int tg_stride;
+  int allow_unscored;
+};
+
+TokenRefs lm_refs(const int32_t* tokens, int T) { return TokenRefs{tokens, T + 1, tokens + 1, T + 1, 0}; }
+
+cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const TokenRefs& tr, uint64_t step, float* losses,
+                                  float* seq_losses) {
   const Plan& p = ctx->plan;
   const hipStream_t s = ctx->stream;
   uint32_t* flags = ctx->at<uint32_t>(p.off_flags);
   uint64_t* seeds = ctx->at<uint64_t>(p.off_seeds);
   float* seq = ctx->at<float>(p.off_seq);
-  const float eps = p.cfg.eps;
+  const float eps = probe_radius(p.cfg);
+  const bool exact = p.cfg.dtype == CDRGE_BF16_EXACT;
 
   CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
     hipLaunchKernelGGL(k_seeds, dim3((p.K + 255) / 256), dim3(256), 0, s, p.cfg.base_seed, step, p.K, seeds);
   }));
   CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
-    hipLaunchKernelGGL(k_check_tokens, dim3(1), dim3(256), 0, s, tokens, p.B * (p.T + 1), p.V, flags);
+    hipLaunchKernelGGL(k_check_tokens, dim3(1), dim3(256), 0, s, tr.in, tr.in_stride, tr.tg, tr.tg_stride, p.B,
+                       p.T, p.V, tr.allow_unscored, flags);
   }));
 
-  const bool bf16 = p.cfg.dtype == CDRGE_BF16;
+  const bool bf16 = p.cfg.dtype != CDRGE_F32;
   if (!bf16) {
     const float* theta = static_cast<const float*>(ctx->params);
     for (const TensorDesc& t : p.tensors) {
@@ -298,7 +329,9 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
   if (bf16) {
     const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
     for (const TensorDesc& t : p.tensors) {
-      if (t.id != static_cast<uint32_t>(1 + 3 * p.L)) continue;  // W_out only; the gate kernels form their own
+      // W_out only (the gate kernels form their own); the exact-perturbation model reads W_out
+      // itself and needs no candidates
+      if (exact || t.id != static_cast<uint32_t>(1 + 3 * p.L)) continue;
       const int64_t n = t.rows * t.cols;
       CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
         hipLaunchKernelGGL(k_pm_table_bf16, dim3(static_cast<uint32_t>((n / 8 + 256) / 256)), dim3(256), 0, s,
@@ -340,7 +373,10 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       }
       m.wt_out = ctx->at<float>(p.off_wt[1 + 3 * p.L]);
       m.sg_out = ctx->at<uint32_t>(p.off_sg[1 + 3 * p.L]);
-      m.tokens = tokens;
+      m.in = tr.in;
+      m.in_stride = tr.in_stride;
+      m.tg = tr.tg;
+      m.tg_stride = tr.tg_stride;
       m.seeds = seeds;
       m.seq_out = seq;
       m.eps = eps;
@@ -365,19 +401,21 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
       uint16_t* emb_m = ctx->at<uint16_t>(p.off_emb_m);
       float* bias_m = ctx->at<float>(p.off_bias_m);
       float* bout_m = ctx->at<float>(p.off_bout_m);
-      auto small = [&](const TensorDesc& t, int out_cols, uint16_t* ob, float* of) {
+      // round: the perturbed value is rounded to bf16 (embedding rows always, as activations of
+      // the first product; biases unless the probe is added exactly)
+      auto small = [&](const TensorDesc& t, int out_cols, uint16_t* ob, float* of, int round) {
         const int groups = static_cast<int>((t.cols + 31) / 32);
         const int64_t n = int64_t(models) * t.rows * groups;
         return timed(ctx, 3, 0.0, [&] {
           hipLaunchKernelGGL(k_model_tensor_bf16, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s,
                              theta + t.off, static_cast<int>(t.rows), static_cast<int>(t.cols), t.id, seeds,
-                             pair0, models, eps, out_cols, ob, of);
+                             pair0, models, eps, out_cols, round, ob, of);
         });
       };
-      CDRGE_TRY(small(p.tensors[0], p.E, emb_m, nullptr));
+      CDRGE_TRY(small(p.tensors[0], p.E, emb_m, nullptr, 1));
       for (int l = 0; l < p.L; ++l)
-        CDRGE_TRY(small(p.tensors[3 + 3 * l], p.L * 4 * p.H, nullptr, bias_m + int64_t(l) * 4 * p.H));
-      CDRGE_TRY(small(p.tensors[2 + 3 * p.L], kCeRows, nullptr, bout_m));
+        CDRGE_TRY(small(p.tensors[3 + 3 * l], p.L * 4 * p.H, nullptr, bias_m + int64_t(l) * 4 * p.H, !exact));
+      CDRGE_TRY(small(p.tensors[2 + 3 * p.L], kCeRows, nullptr, bout_m, !exact));
       for (int l = 0; l < p.L; ++l)
         for (const TensorDesc& t : {p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]}) {
           const int wpr = static_cast<int>(t.cols / 32);
@@ -419,8 +457,8 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           const dim3 xgrid(static_cast<uint32_t>((4 * p.ncols_pad + 255) / 256),
                            static_cast<uint32_t>((p.E / 32 + kGatherChunks - 1) / kGatherChunks));
           CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
-            hipLaunchKernelGGL(k_gather_x0, xgrid, dim3(256), 0, s, emb_m,
-                               tokens, p.B, p.T, t, p.V, p.E, ncols, static_cast<int>(p.ncols_pad), x0);
+            hipLaunchKernelGGL(k_gather_x0, xgrid, dim3(256), 0, s, emb_m, tr.in, tr.in_stride, p.B, t, p.V,
+                               p.E, ncols, static_cast<int>(p.ncols_pad), x0);
           }));
         }
         for (int l = 0; l < p.L; ++l) {
@@ -450,16 +488,22 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
           g.group_cols = group_cols;
           const double flops = 2.0 * 4 * p.H * double(g.in + (g.first ? 0 : p.H)) * ncols;
           CDRGE_TRY(timed(ctx, 0, flops, [&] {
-            hipLaunchKernelGGL(k_lstm_gates_bf16, ggrid, dim3(kGateThreads), kGateLdsBytes, s, g);
+            if (exact)
+              hipLaunchKernelGGL(k_lstm_gates_bf16<true>, ggrid, dim3(kGateThreads), kGateLdsBytes, s, g);
+            else
+              hipLaunchKernelGGL(k_lstm_gates_bf16<false>, ggrid, dim3(kGateThreads), kGateLdsBytes, s, g);
           }));
         }
         CeArgs ce;
         const TensorDesc& tw = p.tensors[1 + 3 * p.L];
-        ce.wp = ctx->at<uint16_t>(p.off_wp[tw.id]);
-        ce.wm = ctx->at<uint16_t>(p.off_wm[tw.id]);
+        // exact perturbation: W_out itself (the kernel adds eps' P), else the two candidates
+        ce.wp = exact ? theta + tw.off : ctx->at<uint16_t>(p.off_wp[tw.id]);
+        ce.wm = exact ? theta + tw.off : ctx->at<uint16_t>(p.off_wm[tw.id]);
+        ce.eps = eps;
         ce.h = hbuf(p.L - 1, t & 1);
         ce.bout_m = bout_m;
-        ce.tokens = tokens;
+        ce.tg = tr.tg;
+        ce.tg_stride = tr.tg_stride;
         ce.seeds = seeds;
         ce.seq = seq;
         ce.pair0 = pair0;
@@ -471,24 +515,30 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
         const double flops = 2.0 * kCeRows * p.H * double(ncols);
         if (p.ce_slices == 1) {
           CDRGE_TRY(timed(ctx, 1, flops, [&] {
-            hipLaunchKernelGGL(k_logits_ce_bf16<false>, cgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
+            if (exact)
+              hipLaunchKernelGGL((k_logits_ce_bf16<false, true>), cgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
+            else
+              hipLaunchKernelGGL((k_logits_ce_bf16<false, false>), cgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
           }));
         } else {
           const dim3 sgrid(cgrid.x, cgrid.y, static_cast<uint32_t>(p.ce_slices));
           CDRGE_TRY(timed(ctx, 1, flops, [&] {
-            hipLaunchKernelGGL(k_logits_ce_bf16<true>, sgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
+            if (exact)
+              hipLaunchKernelGGL((k_logits_ce_bf16<true, true>), sgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
+            else
+              hipLaunchKernelGGL((k_logits_ce_bf16<true, false>), sgrid, dim3(kCeThreads), kCeLdsBytes, s, ce);
           }));
           CDRGE_TRY(timed(ctx, 1, 0.0, [&] {
             hipLaunchKernelGGL(k_ce_reduce, dim3(static_cast<uint32_t>((ncols + 3) / 4)), dim3(256), 0, s,
-                               ctx->at<float>(p.off_zpart), p.ce_slices, ncols, p.B, p.V, p.T, t, bout_m,
-                               tokens, seq);
+                               ctx->at<float>(p.off_zpart), p.ce_slices, ncols, p.B, p.V, t, bout_m,
+                               tr.tg, tr.tg_stride, seq);
           }));
         }
       }
     }
     CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
-      hipLaunchKernelGGL(k_loss_reduce, dim3(models), dim3(256), 0, s, seq, p.B, p.T, 2 * pair0, flags,
-                         losses, seq_losses);
+      hipLaunchKernelGGL(k_loss_reduce, dim3(models), dim3(256), 0, s, seq, p.B, 2 * pair0, flags, losses,
+                         seq_losses);
     }));
   }
   return CDRGE_OK;
@@ -497,7 +547,7 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_
 // The permute-addressed update takes bf16 parameters, K <= 64, all tensors in one launch and
 // 32-bit segment indices within a tensor.
 bool update_perm_ok(const Plan& p) {
-  if (p.cfg.dtype != CDRGE_BF16 || p.K > kUpdPermMaxProbes ||
+  if (p.cfg.dtype == CDRGE_F32 || p.K > kUpdPermMaxProbes ||
       static_cast<int>(p.tensors.size()) > kUpdMaxTensors)
     return false;
   for (const TensorDesc& t : p.tensors)
@@ -513,9 +563,10 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
   CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
     hipLaunchKernelGGL(k_seeds, dim3((p.K + 255) / 256), dim3(256), 0, s, p.cfg.base_seed, step, p.K, seeds);
   }));
+  // eta / (2 K eps) with the radius the probes actually applied
   const float coef = static_cast<float>(static_cast<double>(p.cfg.lr) /
-                                        (2.0 * p.K * static_cast<double>(p.cfg.eps)));
-  const bool bf16 = p.cfg.dtype == CDRGE_BF16;
+                                        (2.0 * p.K * static_cast<double>(probe_radius(p.cfg))));
+  const bool bf16 = p.cfg.dtype != CDRGE_F32;
   const size_t esz = bf16 ? 2 : 4;
   if (p.K <= kUpdLutMaxProbes && static_cast<int>(p.tensors.size()) <= kUpdMaxTensors) {
     // all tensors in one launch (tensor ids are their positions in the flat layout)
@@ -618,9 +669,10 @@ cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   CDRGE_HIP(hipGetDevice(&ctx->device));
   CDRGE_HIP(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, ctx->device));
   if (ctx->n_cu < 1) ctx->n_cu = 1;
-  if (cfg->dtype == CDRGE_BF16) {
-    CDRGE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lstm_gates_bf16),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
+  if (cfg->dtype != CDRGE_F32) {
+    const void* gate = cfg->dtype == CDRGE_BF16_EXACT ? reinterpret_cast<const void*>(k_lstm_gates_bf16<true>)
+                                                      : reinterpret_cast<const void*>(k_lstm_gates_bf16<false>);
+    CDRGE_HIP(hipFuncSetAttribute(gate, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGateLdsBytes)));
     CDRGE_HIP(set_update_lds(ctx, true));
   } else {
     const Plan& p = ctx->plan;
@@ -722,7 +774,14 @@ cdrge_status cdrge_init(cdrge_ctx** ctx_out, const cdrge_config* cfg, void* para
 cdrge_status cdrge_probe_losses(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step, float* losses,
                                 float* seq_losses) {
   if (!ctx || !tokens || !losses) return CDRGE_ERR_INVALID_ARG;
-  return enqueue_probe_losses(ctx, tokens, step, losses, seq_losses);
+  return enqueue_probe_losses(ctx, lm_refs(tokens, ctx->plan.T), step, losses, seq_losses);
+}
+
+cdrge_status cdrge_probe_losses_io(cdrge_ctx* ctx, const int32_t* inputs, const int32_t* targets,
+                                   uint64_t step, float* losses, float* seq_losses) {
+  if (!ctx || !inputs || !targets || !losses) return CDRGE_ERR_INVALID_ARG;
+  const TokenRefs tr{inputs, ctx->plan.T, targets, ctx->plan.T, 1};
+  return enqueue_probe_losses(ctx, tr, step, losses, seq_losses);
 }
 
 cdrge_status cdrge_update(cdrge_ctx* ctx, uint64_t step, const float* losses) {
@@ -732,7 +791,15 @@ cdrge_status cdrge_update(cdrge_ctx* ctx, uint64_t step, const float* losses) {
 
 cdrge_status cdrge_step(cdrge_ctx* ctx, const int32_t* tokens, uint64_t step, float* losses) {
   if (!ctx || !tokens || !losses) return CDRGE_ERR_INVALID_ARG;
-  CDRGE_TRY(enqueue_probe_losses(ctx, tokens, step, losses, nullptr));
+  CDRGE_TRY(enqueue_probe_losses(ctx, lm_refs(tokens, ctx->plan.T), step, losses, nullptr));
+  return enqueue_update(ctx, step, losses);
+}
+
+cdrge_status cdrge_step_io(cdrge_ctx* ctx, const int32_t* inputs, const int32_t* targets, uint64_t step,
+                           float* losses) {
+  if (!ctx || !inputs || !targets || !losses) return CDRGE_ERR_INVALID_ARG;
+  const TokenRefs tr{inputs, ctx->plan.T, targets, ctx->plan.T, 1};
+  CDRGE_TRY(enqueue_probe_losses(ctx, tr, step, losses, nullptr));
   return enqueue_update(ctx, step, losses);
 }
 
@@ -834,7 +901,7 @@ cdrge_status cdrge_step_noalloc(const cdrge_config* cfg, void* params, const int
   ctx.ws = static_cast<char*>(ws);
   ctx.stream = static_cast<hipStream_t>(stream);
   CDRGE_TRY(init_device(&ctx, cfg));  // clears the status words the previous call left
-  CDRGE_TRY(enqueue_probe_losses(&ctx, tokens, step, losses, nullptr));
+  CDRGE_TRY(enqueue_probe_losses(&ctx, lm_refs(tokens, ctx.plan.T), step, losses, nullptr));
   return enqueue_update(&ctx, step, losses);
 }
 

@@ -3,7 +3,8 @@
 // (W_out +- eps P) h_t + (b_out +- eps p), then the softmax cross-entropy against the next token
 // (the pages' next-character objective: pith.science review, Figure 2 caption) accumulated per
 // sequence. The perturbed output weights are formed exactly as in the gate kernel: a per-element
-// bit select between the candidates bf16(W + eps) and bf16(W - eps).
+// bit select between the candidates bf16(W + eps) and bf16(W - eps), or, for the
+// exact-perturbation model, W and the operand eps' P multiplied into the same accumulators.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,17 +52,22 @@ struct CeArgs {
   const uint16_t* wm;      // W_out candidates [V][H]
   const uint16_t* h;       // last layer h_t, [H / 32][ncols_pad][32] (k-chunk-major)
   const float* bout_m;     // per-model perturbed output bias [2P][64]
-  const int32_t* tokens;   // [B][T+1]
+  const int32_t* tg;       // target of (b, t) at tg[b * tg_stride + t]; below zero: not scored
+  int tg_stride;
   const uint64_t* seeds;
   float* seq;              // [2P][B]
   float* zpart;            // split: partial logits [slices][2P B][64]
   int pair0, H, B, V, T, t, ncols_pad;
   int kper;                // split: 32-wide chunks per slice (a multiple of 4)
   uint32_t tensor_wout;
+  float eps;               // exact perturbation: the radius eps' (a bf16 value)
 };
 
 // grid: (ceil(B / 128), pairs in chunk, slices)
-template <bool kSplit>
+// kExact (exact-perturbation bf16): wp = wm = W_out itself; the LDS tile of side 0 holds W_out, that
+// of side 1 the bf16 operand eps' P, and each wave multiplies both into its accumulators, the
+// -eps model with the sign bits of eps' P flipped in registers: (W +- eps' P) h = W h +- eps' P h.
+template <bool kSplit, bool kExact>
 __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* As = smem;                                  // [buf][side][64][40]
@@ -94,10 +100,12 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         rp[k] = frow_ok ? reinterpret_cast<const uint4*>(wp)[k] : make_uint4(0, 0, 0, 0);
-        rm[k] = frow_ok ? reinterpret_cast<const uint4*>(wm)[k] : make_uint4(0, 0, 0, 0);
+        if constexpr (!kExact) rm[k] = frow_ok ? reinterpret_cast<const uint4*>(wm)[k] : make_uint4(0, 0, 0, 0);
       }
     }
   };
+  // bf16 bits of eps' in both halves of a word (the exact-perturbation operand before signs)
+  const uint32_t eps2 = (__float_as_uint(a.eps) >> 16) * 0x00010001u;
   // h fragments of chunk c (clamped to the last chunk of the range)
   auto load_h = [&](int c, bf16x8 (&b)[4]) {
     const uint16_t* src = hlane + hchunk * min(c, c_end - 1);
@@ -117,8 +125,13 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const uint32_t mask = pair_mask(w, m);
-        plus[m] = (mask & m32[m]) | (~mask & p32[m]);
-        minus[m] = (mask & p32[m]) | (~mask & m32[m]);
+        if constexpr (kExact) {
+          plus[m] = p32[m];                                    // W
+          minus[m] = frow_ok ? eps2 | (mask & 0x80008000u) : 0u;  // eps' P (padding rows zero)
+        } else {
+          plus[m] = (mask & m32[m]) | (~mask & p32[m]);
+          minus[m] = (mask & p32[m]) | (~mask & m32[m]);
+        }
       }
       uint4* ap = reinterpret_cast<uint4*>(As + ((buf * 2 + 0) * kCeRows + tid) * kCeLdsStride);
       uint4* am = reinterpret_cast<uint4*>(As + ((buf * 2 + 1) * kCeRows + tid) * kCeLdsStride);
@@ -135,14 +148,31 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t pflip = side ? 0x80008000u : 0u;  // the -eps model's sign of eps' P
   auto mma = [&](int buf, const bf16x8 (&bfr)[4]) {
-    const uint16_t* A = As + ((buf * 2 + side) * kCeRows + (lane & 15)) * kCeLdsStride + 8 * (lane >> 4);
+    if constexpr (kExact) {
+      const uint16_t* AW = As + ((buf * 2 + 0) * kCeRows + (lane & 15)) * kCeLdsStride + 8 * (lane >> 4);
+      const uint16_t* AP = As + ((buf * 2 + 1) * kCeRows + (lane & 15)) * kCeLdsStride + 8 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 afr = *reinterpret_cast<const bf16x8*>(A + 16 * i * kCeLdsStride);
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 aw = *reinterpret_cast<const bf16x8*>(AW + 16 * i * kCeLdsStride);
+        const u32x4 ap = *reinterpret_cast<const u32x4*>(AP + 16 * i * kCeLdsStride) ^ pflip;
+        const bf16x8 apf = __builtin_bit_cast(bf16x8, ap);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apf, bfr[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    } else {
+      const uint16_t* A = As + ((buf * 2 + side) * kCeRows + (lane & 15)) * kCeLdsStride + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 afr = *reinterpret_cast<const bf16x8*>(A + 16 * i * kCeLdsStride);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+      }
     }
   };
 
@@ -192,8 +222,8 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
     const int n = 64 * ch + 16 * j + (lane & 15);
     const int b = bcol0 + n;
     const bool ok = b < a.B;
-    int y = ok ? a.tokens[static_cast<int64_t>(b) * (a.T + 1) + a.t + 1] : 0;
-    y = min(max(y, 0), a.V - 1);
+    const int y_raw = ok ? a.tg[static_cast<int64_t>(b) * a.tg_stride + a.t] : 0;
+    const int y = min(y_raw, a.V - 1);
     float z[16];
     float zmax = -INFINITY;
 #pragma unroll
@@ -221,7 +251,7 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
     zy += __shfl_xor(zy, 16);
     zy += __shfl_xor(zy, 32);
     if (ok && g == 0) {
-      const float l = (zmax + __logf(sum)) - zy;
+      const float l = (y_raw >= 0) ? (zmax + __logf(sum)) - zy : 0.f;
       float* dst = a.seq + static_cast<int64_t>(m) * a.B + b;
       *dst = (a.t == 0) ? l : *dst + l;
     }
@@ -230,11 +260,13 @@ __global__ __launch_bounds__(kCeThreads) void k_logits_ce_bf16(CeArgs a) {
 
 // Finishes the split logits: one wave per (model, sequence) column of the chunk, lane = logit
 // row. z = bout + sum over slices (in slice order) of the partials, then the softmax
-// cross-entropy against the next token, accumulated into seq[m][b] over t.
+// cross-entropy against the target of (b, t) (none when it is below zero), accumulated into
+// seq[m][b] over t.
 // grid: ceil(2P B / 4) blocks of 256 threads.
 __global__ __launch_bounds__(256) void k_ce_reduce(const float* __restrict__ zpart, int slices, int ncols,
-                                                   int B, int V, int T, int t, const float* __restrict__ bout_m,
-                                                   const int32_t* __restrict__ tokens, float* __restrict__ seq) {
+                                                   int B, int V, int t, const float* __restrict__ bout_m,
+                                                   const int32_t* __restrict__ tg, int tg_stride,
+                                                   float* __restrict__ seq) {
   const int lane = threadIdx.x & 63;
   const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (col >= ncols) return;
@@ -248,11 +280,11 @@ __global__ __launch_bounds__(256) void k_ce_reduce(const float* __restrict__ zpa
   float e = row_ok ? __expf(z - zmax) : 0.f;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
-  int y = tokens[static_cast<int64_t>(b) * (T + 1) + t + 1];
-  y = min(max(y, 0), V - 1);
+  const int y_raw = tg[static_cast<int64_t>(b) * tg_stride + t];
+  const int y = min(max(y_raw, 0), V - 1);
   const float zy = __shfl(z, y);
   if (lane == 0) {
-    const float l = (zmax + __logf(e)) - zy;
+    const float l = (y_raw >= 0) ? (zmax + __logf(e)) - zy : 0.f;
     float* dst = seq + static_cast<int64_t>(m) * B + b;
     *dst = (t == 0) ? l : *dst + l;
   }

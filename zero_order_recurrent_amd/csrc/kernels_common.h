@@ -50,19 +50,37 @@ __global__ void k_seeds(uint64_t base_seed, uint64_t step, int n, uint64_t* seed
   if (i < n) seeds[i] = probe_seed(base_seed, step, static_cast<uint32_t>(i));
 }
 
-// flags[1] = 1 if any token lies outside [0, V), else 0. One block.
-__global__ void k_check_tokens(const int32_t* tokens, int n, int V, uint32_t* flags) {
+// Checks one step's inputs and targets and counts the positions that are scored. Input (b, t)
+// is in[b * in_stride + t], target (b, t) is tg[b * tg_stride + t]; a target below zero marks a
+// position that is not scored, which only the transduction form allows (allow_unscored).
+// flags[1] = 1 if an input lies outside [0, V), a target at or above V, or (when unscored targets
+// are not allowed) below zero; else 0. flags[2] = number of scored positions. One block.
+__global__ void k_check_tokens(const int32_t* __restrict__ in, int in_stride, const int32_t* __restrict__ tg,
+                               int tg_stride, int B, int T, int V, int allow_unscored, uint32_t* flags) {
   __shared__ int bad;
-  if (threadIdx.x == 0) bad = 0;
+  __shared__ unsigned int scored;
+  if (threadIdx.x == 0) {
+    bad = 0;
+    scored = 0u;
+  }
   __syncthreads();
   int mine = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int v = tokens[i];
-    mine |= (v < 0 || v >= V) ? 1 : 0;
+  unsigned int count = 0u;
+  const int64_t n = static_cast<int64_t>(B) * T;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t b = i / T, t = i - b * T;
+    const int x = in[b * in_stride + t];
+    const int y = tg[b * tg_stride + t];
+    mine |= (x < 0 || x >= V || y >= V || (y < 0 && !allow_unscored)) ? 1 : 0;
+    count += (y >= 0) ? 1u : 0u;
   }
   if (mine) atomicOr(&bad, 1);
+  atomicAdd(&scored, count);
   __syncthreads();
-  if (threadIdx.x == 0) flags[1] = static_cast<uint32_t>(bad);
+  if (threadIdx.x == 0) {
+    flags[1] = static_cast<uint32_t>(bad);
+    flags[2] = scored;
+  }
 }
 
 // The two probe-independent candidates of every bf16 weight: wp = bf16(w + eps), wm = bf16(w - eps).
@@ -120,10 +138,11 @@ __global__ void k_sign_words(const uint64_t* __restrict__ seeds, int pair0, int 
 // Per-model perturbed copy of a small tensor [rows][cols] of a bf16 model, for models
 // m = 0..2P-1 of a chunk (model 2q is probe pair0+q at +eps, 2q+1 the same probe at -eps).
 // out_bf16 (if not null) gets bf16 bits at [m][r][out_cols]; out_f32 (if not null) gets the same
-// values as floats. One thread per (m, r, 32-column group).
+// values as floats, or, when `round` is 0, the perturbed value w +- eps itself in float (the
+// exact-perturbation model's biases). One thread per (m, r, 32-column group).
 __global__ void k_model_tensor_bf16(const uint16_t* __restrict__ src, int rows, int cols,
                                     uint32_t tensor, const uint64_t* __restrict__ seeds, int pair0,
-                                    int n_models, float eps, int out_cols,
+                                    int n_models, float eps, int out_cols, int round,
                                     uint16_t* __restrict__ out_bf16, float* __restrict__ out_f32) {
   const int groups = (cols + 31) / 32;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -139,24 +158,26 @@ __global__ void k_model_tensor_bf16(const uint16_t* __restrict__ src, int rows, 
     const int c = g * 32 + j;
     if (c >= cols) break;
     const uint32_t bit = (word >> sign_bit_pos(static_cast<uint32_t>(c))) & 1u;
-    const uint32_t v = perturb_bf16(src[static_cast<int64_t>(r) * cols + c], signed_eps(e, bit));
+    const uint32_t w16 = src[static_cast<int64_t>(r) * cols + c];
+    const float se = signed_eps(e, bit);
+    const uint32_t v = perturb_bf16(w16, se);
     const int64_t o_idx = (static_cast<int64_t>(m) * rows + r) * out_cols + c;
     if (out_bf16) out_bf16[o_idx] = static_cast<uint16_t>(v);
-    if (out_f32) out_f32[o_idx] = bf16_to_f32(v);
+    if (out_f32) out_f32[o_idx] = round ? bf16_to_f32(v) : bf16_to_f32(w16) + se;
   }
 }
 
 // Layer-0 input of timestep t for every (model, sequence) column of a chunk: column m * B + b
 // holds emb_m[m][token(b, t)][:], the model's perturbed embedding row, stored k-chunk-major
-// like the h of a lower layer (element (column, e) at ((e / 32) ncols_pad + column) 32 + e % 32).
-// Columns ncols .. ncols_pad - 1 are zero. Tokens outside [0, V) are clamped (the step's losses
-// are NaN then anyway). E % 32 == 0. A thread owns one 16-byte piece of one column in each of
+// like the h of a lower layer (element (column, e) at ((e / 32) ncols_pad + column) 32 + e % 32);
+// the token of sequence b at t is in[b * in_stride + t]. Columns ncols .. ncols_pad - 1 are zero.
+// Tokens outside [0, V) are clamped (the step's losses are NaN then anyway). E % 32 == 0. A thread owns one 16-byte piece of one column in each of
 // kGatherChunks consecutive 32-wide chunks (one token lookup for all of them, and their loads in
 // flight together); grid (ceil(4 ncols_pad / 256), ceil(E / 32 / kGatherChunks)), and consecutive
 // threads write consecutive pieces of a chunk.
 constexpr int kGatherChunks = 4;
-__global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* __restrict__ tokens, int B,
-                            int T, int t, int V, int E, int ncols, int ncols_pad, uint16_t* __restrict__ x) {
+__global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* __restrict__ in, int in_stride,
+                            int B, int t, int V, int E, int ncols, int ncols_pad, uint16_t* __restrict__ x) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;  // 4 column + piece, < 4 ncols_pad
   if (i >= 4u * static_cast<uint32_t>(ncols_pad)) return;
   const uint32_t col = i >> 2, p4 = i & 3, kc0 = blockIdx.y * kGatherChunks;
@@ -165,7 +186,7 @@ __global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* _
   const uint4* row = nullptr;
   if (col < static_cast<uint32_t>(ncols)) {
     const uint32_t m = col / static_cast<uint32_t>(B), b = col - m * static_cast<uint32_t>(B);
-    int tok = tokens[static_cast<int64_t>(b) * (T + 1) + t];
+    int tok = in[static_cast<int64_t>(b) * in_stride + t];
     tok = min(max(tok, 0), V - 1);
     row = reinterpret_cast<const uint4*>(emb_m + (static_cast<int64_t>(m) * V + tok) * E);
   }
@@ -181,9 +202,10 @@ __global__ void k_gather_x0(const uint16_t* __restrict__ emb_m, const int32_t* _
   }
 }
 
-// losses[m0 + m] = (sum_b seq[m][b]) / (B T) with a fixed-order double reduction (bitwise
-// repeatable); seq_out[m0 + m][b] = seq[m][b] when requested. NaN when tokens were invalid.
-__global__ void k_loss_reduce(const float* __restrict__ seq, int B, int T, int m0,
+// losses[m0 + m] = (sum_b seq[m][b]) / (number of scored positions, flags[2]; B T for a language
+// model) with a fixed-order double reduction (bitwise repeatable); seq_out[m0 + m][b] = seq[m][b]
+// when requested. NaN when tokens were invalid or no position is scored.
+__global__ void k_loss_reduce(const float* __restrict__ seq, int B, int m0,
                               const uint32_t* __restrict__ flags, float* __restrict__ losses,
                               float* __restrict__ seq_out) {
   __shared__ double part[256];
@@ -201,8 +223,8 @@ __global__ void k_loss_reduce(const float* __restrict__ seq, int B, int T, int m
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const float mean = static_cast<float>(part[0] / (static_cast<double>(B) * T));
-    losses[m0 + m] = flags[1] ? __builtin_nanf("") : mean;
+    const float mean = static_cast<float>(part[0] / static_cast<double>(flags[2]));
+    losses[m0 + m] = (flags[1] || flags[2] == 0u) ? __builtin_nanf("") : mean;
   }
 }
 

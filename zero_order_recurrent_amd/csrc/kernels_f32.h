@@ -66,7 +66,9 @@ struct F32Args {
   const uint32_t* sg_ih[kF32MaxLayers];     // sign words [pairs][ceil(in_l / 32)][4H]
   const uint32_t* sg_hh[kF32MaxLayers];     // [pairs][ceil(H / 32)][4H]
   const uint32_t* sg_out;                   // [pairs][ceil(H / 32)][V]
-  const int32_t* tokens;                    // [B][T+1]
+  const int32_t* in;                        // input of (b, t) at in[b * in_stride + t]
+  const int32_t* tg;                        // target at tg[b * tg_stride + t]; below zero: not scored
+  int in_stride, tg_stride;
   const uint64_t* seeds;                    // all K seeds
   float* seq_out;                           // [2 pc][B]: per (model, sequence) sum over t of the CE
   float eps;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
       const int g = slot / (2 * NB), s = (slot / NB) & 1, b = slot % NB;
       float v = 0.f;
       if (b < nb) {
-        int tok = a.tokens[static_cast<int64_t>(b0 + b) * (a.T + 1) + t];
+        int tok = a.in[static_cast<int64_t>(b0 + b) * a.in_stride + t];
         tok = min(max(tok, 0), V - 1);  // invalid tokens are reported through the loss (NaN)
         const PhiloxOut o = sign_block(seed[g], 0u, static_cast<uint32_t>(tok), static_cast<uint32_t>(e >> 7));
         const uint32_t bit = (pick_word(o, (e >> 5) & 3) >> sign_bit_pos(e)) & 1u;
@@ -368,9 +370,8 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
         for (int v = 1; v < V; ++v) zmax = fmaxf(zmax, z[v * M + slot]);
         float sum = 0.f;
         for (int v = 0; v < V; ++v) sum += expf(z[v * M + slot] - zmax);
-        int y = a.tokens[static_cast<int64_t>(b0 + b) * (a.T + 1) + t + 1];
-        y = min(max(y, 0), V - 1);
-        loss[slot] += (zmax + logf(sum)) - z[y * M + slot];
+        const int y = a.tg[static_cast<int64_t>(b0 + b) * a.tg_stride + t];
+        if (y >= 0) loss[slot] += (zmax + logf(sum)) - z[min(y, V - 1) * M + slot];
       }
     }
   }

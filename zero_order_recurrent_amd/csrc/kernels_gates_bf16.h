@@ -142,6 +142,13 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
   pr = cw / a.n_col_blocks;
 }
 
+// kExact (exact-perturbation bf16): stage half 0 holds the stored weights W and half 1 the bf16
+// operand eps' P (eps' = a.eps, a bf16 value; P = +-1 from the sign words); every wave multiplies
+// both into its accumulators, the -eps model with the sign bits of eps' P flipped in registers,
+// so that G = W [x; h] +- eps' P [x; h] with no rounding of the perturbed weight. Twice the
+// matrix-core work; A fragments are read one row group ahead (two rings of two) to stay within
+// the register budget of two waves per SIMD.
+template <bool kExact>
 __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
   char* As = reinterpret_cast<char*>(smem);  // [8 stages][model][128 rows][64 B], swizzled
@@ -194,12 +201,25 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // bf16(w + eps) and bf16(w - eps) are formed here (one float add each, then the packed
   // round-to-nearest-even conversion) and the sign bit picks one per model.
   const float eps = a.eps;
+  const uint32_t eps2 = (__float_as_uint(eps) >> 16) * 0x00010001u;  // bf16 eps' in both halves
   auto form_w = [&](const uint4& wv, uint32_t word, int stage) {
     // Piece q covers columns 8q..8q+7 of the 32-column word: pairs 4q..4q+3, which read bits
     // 4q+p (even column) and 16+4q+p (odd column).
     const uint32_t t4 = word >> (4 * q);
     const uint32_t w2[4] = {wv.x, wv.y, wv.z, wv.w};
     uint32_t plus[4], minus[4];
+    if constexpr (kExact) {
+      // half 0: W as stored; half 1: eps' P (sign bit set where the probe sign is -1)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        plus[p] = w2[p];
+        minus[p] = eps2 | ((t4 << (15 - p)) & 0x80008000u);
+      }
+      char* st = As + stage * kAStageBytes;
+      *reinterpret_cast<uint4*>(st + piece_offset(ra, q)) = make_uint4(plus[0], plus[1], plus[2], plus[3]);
+      *reinterpret_cast<uint4*>(st + piece_offset(kTileRows + ra, q)) = make_uint4(minus[0], minus[1], minus[2], minus[3]);
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const float lo = __uint_as_float(w2[p] << 16), hi = __uint_as_float(w2[p] & 0xffff0000u);
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // before it is multiplied (row groups 0-1 of the next chunk at the end of the current one).
   bf16x8 afr[4];
   bf16x8 bq[kBRing][4];
-  const int a_lane_off = piece_offset(side * kTileRows + (lane & 15), kp);
+  const int a_lane_off = piece_offset((kExact ? 0 : side * kTileRows) + (lane & 15), kp);
   auto read_a = [&](int stage, int i, bf16x8& dst) {
     // row group i: 16 * i rows further, i.e. 1024 * i bytes (the swizzle repeats every 16 rows)
     dst = *reinterpret_cast<const bf16x8*>(As + stage * kAStageBytes + a_lane_off + 1024 * i);
@@ -233,6 +253,14 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   auto mma_group = [&](int i, const bf16x8& af, const bf16x8 (&b)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[j], acc[i][j], 0, 0, 0);
+  };
+  // exact: W fragment in afr[2 (i % 2)], eps' P fragment (signs flipped for the -eps model) in
+  // afr[2 (i % 2) + 1]; eps' P lies kTileRows rows (8 KB) after W, with the same swizzle
+  const uint32_t pflip = side ? 0x80008000u : 0u;
+  auto read_a2 = [&](int stage, int i, bf16x8& dw, bf16x8& dp) {
+    const char* base = As + stage * kAStageBytes + a_lane_off + 1024 * i;
+    dw = *reinterpret_cast<const bf16x8*>(base);
+    dp = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + kTileRows * 64) ^ pflip);
   };
   // Activations of chunk c (clamped to the last one): fragment j is the 16 columns
   // 16 j .. 16 j + 15 of the wave, 512 elements further per fragment.
@@ -279,9 +307,17 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      mma_group(i, afr[i % 4], bq[s_]);
-      if (i + 2 < 8) read_a(rs, i + 2, afr[(i + 2) % 4]);
-      else read_a(rs1, i - 6, afr[(i + 2) % 4]);
+      if constexpr (kExact) {
+        const int cur = 2 * (i % 2), nxt = 2 * ((i + 1) % 2);
+        mma_group(i, afr[cur], bq[s_]);
+        mma_group(i, afr[cur + 1], bq[s_]);
+        if (i + 1 < 8) read_a2(rs, i + 1, afr[nxt], afr[nxt + 1]);
+        else read_a2(rs1, 0, afr[nxt], afr[nxt + 1]);
+      } else {
+        mma_group(i, afr[i % 4], bq[s_]);
+        if (i + 2 < 8) read_a(rs, i + 2, afr[(i + 2) % 4]);
+        else read_a(rs1, i - 6, afr[(i + 2) % 4]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (i == 5) {
         form_w(w_r[wuse], wd_r[wuse], ws);
@@ -314,8 +350,12 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     for (int k = 0; k < 4; ++k) form_w(wp[k], dp[k], k);
   }
   __syncthreads();
-  read_a(0, 0, afr[0]);
-  read_a(0, 1, afr[1]);
+  if constexpr (kExact) {
+    read_a2(0, 0, afr[0], afr[1]);
+  } else {
+    read_a(0, 0, afr[0]);
+    read_a(0, 1, afr[1]);
+  }
 
   static_assert(kBRing == 4, "the step is unrolled for a ring of 4");
   int c = 0;
