@@ -283,12 +283,14 @@ def test_resume_equals_uninterrupted():
     run.close()
 
 
-@pytest.mark.parametrize("hidden,pairs", [(256, 32), (512, 16), (256, 12), (768, 8)])
+@pytest.mark.parametrize("hidden,pairs", [(256, 32), (512, 16), (256, 12), (768, 8), (1024, 6), (640, 10), (544, 8)])
 def test_xcd_grouped_tile_order(oracle, hidden, pairs):
-    # H = 256: 8 row tiles and 32 pairs x 1 column block, grouped 8 x 4 per XCD; H = 512: 16 row
-    # tiles and 16 pairs, grouped 16 x 2. H = 256 with 12 pairs: 96 workgroups, three 8 x 4 groups
-    # over the 8 XCDs (12 workgroups each), so groups straddle XCDs. H = 768: 24 row tiles, so
-    # each pair of column blocks has one 16 x 2 group and a short 8 x 2 one.
+    # B = 256 (one column block per model). H = 256: 8 row tiles and 32 pairs, grouped 8 x 4 per
+    # XCD; H = 512: 16 row tiles and 16 pairs, grouped 16 x 2; H = 256 with 12 pairs: 96
+    # workgroups, three 8 x 4 groups over the 8 XCDs (12 workgroups each), so groups straddle XCDs;
+    # H = 768: 24 row tiles, so each pair of column blocks has one 16 x 2 group and a short 8 x 2
+    # one; H = 1024 with 6 pairs: 16 x 2 groups, 24 workgroups per XCD; H = 640 and 544: 20 and 17
+    # row tiles, short groups of 4 x 2 and 1 x 2.
     c = b.make_config(1, 50, 64, hidden, 256, 2, pairs, "bf16", 1e-3, 1e-3, 82)
     say(f"[gpu] xcd-grouped tile order, H={hidden}")
     theta, tokens = _inputs(c, 12)
