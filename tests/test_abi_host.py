@@ -114,6 +114,6 @@ def test_noalloc_entry_point_rejects_before_any_device_work(lib):
     small = b.config_from_preset(PRESETS["tiny"])
     assert b.cdrge_workspace_bytes(small) <= 64 << 20
     assert lib.cdrge_step_noalloc(b.ctypes.byref(small), None, fake, 0, fake, None) == 1
-    # the largest probe chunk of the char-LM shape that fits
-    fits = b.make_config(2, 50, 128, 1024, 1024, 10, 64, "bf16", 1e-4, 1e-4, 3003, probes_per_chunk=1)
+    # the char-LM model at 768 sequences, one probe pair per chunk, fits
+    fits = b.make_config(2, 50, 128, 1024, 768, 10, 64, "bf16", 1e-4, 1e-4, 3003, probes_per_chunk=1)
     assert b.cdrge_workspace_bytes(fits) <= 64 << 20

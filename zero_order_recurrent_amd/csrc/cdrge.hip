@@ -76,6 +76,7 @@ struct Plan {
   std::vector<size_t> off_wp, off_wm;  // per tensor id (bf16 matrices only)
   std::vector<size_t> off_sg;          // per tensor id (W_ih, W_hh; fp32 also W_out): sign words of a chunk
   std::vector<size_t> off_wt;          // per tensor id (fp32 W_ih, W_hh, W_out): k-major copy W^T
+  std::vector<size_t> off_wtile;       // per tensor id (bf16 W_ih, W_hh): tile-major copy for the gate kernel
   int f32_g, f32_nb, f32_threads;      // fp32: pairs and sequences per workgroup, threads
   int ce_slices, ce_kper;              // bf16 logits: K slices (1 = fused) and 32-wide chunks per slice
   size_t off_zpart;                    // bf16 logits: partial logits when split
@@ -168,6 +169,7 @@ Plan make_plan(const cdrge_config* c) {
   p.off_wm.assign(p.tensors.size(), 0);
   p.off_sg.assign(p.tensors.size(), 0);
   p.off_wt.assign(p.tensors.size(), 0);
+  p.off_wtile.assign(p.tensors.size(), 0);
   p.ce_slices = 1;
   p.ce_kper = 0;
   p.off_zpart = 0;
@@ -184,8 +186,10 @@ Plan make_plan(const cdrge_config* c) {
       p.off_wm[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
     }
     for (int l = 0; l < p.L; ++l)
-      for (const TensorDesc& t : {p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]})
+      for (const TensorDesc& t : {p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]}) {
         p.off_sg[t.id] = region(sizeof(uint32_t) * p.P * t.rows * (t.cols / 32));
+        p.off_wtile[t.id] = region(sizeof(uint16_t) * t.rows * t.cols);
+      }
     p.off_emb_m = region(sizeof(uint16_t) * models * p.V * p.E);
     p.off_bias_m = region(sizeof(float) * models * p.L * 4 * p.H);
     p.off_bout_m = region(sizeof(float) * models * kCeRows);
@@ -328,6 +332,16 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const TokenRefs& tr, uint64_t 
   }
   if (bf16) {
     const uint16_t* theta = static_cast<const uint16_t*>(ctx->params);
+    // tile-major copies of the gate weights, read by every gate launch of this call
+    for (int l = 0; l < p.L; ++l)
+      for (const TensorDesc& t : {p.tensors[1 + 3 * l], p.tensors[2 + 3 * l]}) {
+        const int64_t pieces = t.rows * t.cols / 8;
+        const uint32_t blocks = static_cast<uint32_t>(std::min<int64_t>((pieces + 255) / 256, int64_t(1) << 20));
+        CDRGE_TRY(timed(ctx, 3, 0.0, [&] {
+          hipLaunchKernelGGL(k_tile_gate_weights, dim3(blocks), dim3(256), 0, s, theta + t.off, p.H,
+                             static_cast<int>(t.cols), ctx->at<uint16_t>(p.off_wtile[t.id]));
+        }));
+      }
     for (const TensorDesc& t : p.tensors) {
       // W_out only (the gate kernels form their own); the exact-perturbation model reads W_out
       // itself and needs no candidates
@@ -465,8 +479,8 @@ cdrge_status enqueue_probe_losses(cdrge_ctx* ctx, const TokenRefs& tr, uint64_t 
           GateArgs g;
           const TensorDesc& tih = p.tensors[1 + 3 * l];
           const TensorDesc& thh = p.tensors[2 + 3 * l];
-          g.w_ih = theta + tih.off;
-          g.w_hh = theta + thh.off;
+          g.w_ih = ctx->at<uint16_t>(p.off_wtile[tih.id]);
+          g.w_hh = ctx->at<uint16_t>(p.off_wtile[thh.id]);
           g.eps = eps;
           g.sg_ih = ctx->at<uint32_t>(p.off_sg[tih.id]);
           g.sg_hh = ctx->at<uint32_t>(p.off_sg[thh.id]);

@@ -25,9 +25,10 @@
 //   * activations (stored k-chunk-major, so a 16-column fragment is 1 KB of contiguous memory)
 //     go straight from global memory into the MFMA operand registers of the wave that uses them
 //     (each column belongs to one wave), in a 4-deep register ring, three chunks ahead;
-//   * the stored weights and sign words of chunks c+5 and c+6 are requested together in odd
-//     steps (both halves of each row's 128-byte line back to back) into a register ring, and
-//     chunk c+4 is selected into LDS in step c, after row group 5;
+//   * the stored weights (read from a tile-major copy, in which a tile's 128 rows of one chunk
+//     are 8 KB of contiguous memory) and sign words of chunks c+5 and c+6 are requested together
+//     in odd steps into a register ring, and chunk c+4 is selected into LDS in step c, after row
+//     group 5;
 //   * the selected tiles of both models live in an 8-stage LDS ring; fragments are read two row
 //     groups ahead of the MFMAs that use them; a barrier follows the select in every fourth step.
 // The cell state stays in accumulator order (tile-private, 16 bytes per lane and row group), and
@@ -93,8 +94,8 @@ __device__ __forceinline__ int piece_offset(int r, int p) {
 }
 
 struct GateArgs {
-  const uint16_t* w_ih;    // W_ih [4H][in], bf16 parameters
-  const uint16_t* w_hh;    // W_hh [4H][H]
+  const uint16_t* w_ih;    // W_ih [4H][in], bf16 parameters, in the tile-major copy of k_tile_gate_weights
+  const uint16_t* w_hh;    // W_hh [4H][H], likewise
   const uint32_t* sg_ih;   // sign words of W_ih for the chunk's pairs, [pairs][in / 32][4H]
   const uint32_t* sg_hh;   // sign words of W_hh, [pairs][H / 32][4H]
   const uint16_t* x_in;    // input of this layer at t, [in / 32][ncols_pad][32] (k-chunk-major)
@@ -142,6 +143,25 @@ __device__ __forceinline__ void gate_tile_of_block(const GateArgs& a, int& rt, i
   pr = cw / a.n_col_blocks;
 }
 
+// Tile-major copy of one gate weight matrix W [4H][cols] (bf16, cols a multiple of 32) for
+// k_lstm_gates_bf16. Block (rt, cc) holds row tile rt (its local row 4u + g is gate g of unit
+// 32 rt + u, i.e. row g H + 32 rt + u of W) and columns 32 cc .. 32 cc + 31, row-major: 128 x 32
+// values, 8 KB of contiguous memory; blocks are ordered rt-major. One thread per 16 bytes.
+__global__ void k_tile_gate_weights(const uint16_t* __restrict__ w, int H, int cols, uint16_t* __restrict__ wt) {
+  const int nch = cols / kKChunk;
+  const int64_t pieces = int64_t(4) * H * cols / 8;
+  for (int64_t o = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; o < pieces;
+       o += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t blk = o >> 9;  // 512 pieces per block
+    const int pc = static_cast<int>(o & 511);
+    const int rt = static_cast<int>(blk / nch), cc = static_cast<int>(blk - int64_t(rt) * nch);
+    const int ra = pc >> 2, q = pc & 3;
+    const int64_t row = int64_t(ra & 3) * H + int64_t(kUnitsPerTile) * rt + (ra >> 2);
+    *reinterpret_cast<uint4*>(wt + 8 * o) =
+        *reinterpret_cast<const uint4*>(w + row * cols + int64_t(kKChunk) * cc + 8 * q);
+  }
+}
+
 // kExact (exact-perturbation bf16): stage half 0 holds the stored weights W and half 1 the bf16
 // operand eps' P (eps' = a.eps, a bf16 value; P = +-1 from the sign words); every wave multiplies
 // both into its accumulators, the -eps model with the sign bits of eps' P flipped in registers,
@@ -167,8 +187,14 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   const int q = tid & 3;
   const int ra = tid >> 2;
   const int grow = (ra & 3) * H + u0 + (ra >> 2);
-  const uint32_t woff_x = static_cast<uint32_t>(grow * a.in + 8 * q);
-  const uint32_t woff_h = static_cast<uint32_t>(grow * H + 8 * q);
+  // Weights come from the tile-major copies (k_tile_gate_weights): the 128 rows x 32 columns of
+  // this row tile and one chunk are 8 KB of contiguous memory, and this thread's 16 bytes (row ra,
+  // columns 8q..8q+7) are at element 8 tid of the block, so each wave reads 1 KB of contiguous
+  // weights per chunk (eight whole cache lines rather than sixteen halves).
+  // (a wave-uniform base per chunk plus a 32-bit per-lane byte offset)
+  const char* wt_x = reinterpret_cast<const char*>(a.w_ih + static_cast<int64_t>(rt) * (a.in / kKChunk) * kTileRows * kKChunk);
+  const char* wt_h = reinterpret_cast<const char*>(a.w_hh + static_cast<int64_t>(rt) * (H / kKChunk) * kTileRows * kKChunk);
+  const uint32_t wt_lane = 16u * static_cast<uint32_t>(tid);
   // sign words of row grow for this pair: one 32-bit word per 32-column chunk, chunk-major, so
   // the 128 rows of a tile read 4 runs of 32 consecutive words per chunk
   const uint32_t* sgx = a.sg_ih + static_cast<int64_t>(pr) * (a.in / kKChunk) * (4 * H) + grow;
@@ -192,8 +218,8 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   auto load_w = [&](int c, uint4& w_out, uint32_t& word_out) {
     const bool xpart = c < kx;
     const int cc = xpart ? c : c - kx;
-    const uint16_t* w = (xpart ? a.w_ih : a.w_hh) + kKChunk * cc;
-    w_out = *reinterpret_cast<const uint4*>(w + (xpart ? woff_x : woff_h));
+    const char* w = (xpart ? wt_x : wt_h) + static_cast<int64_t>(cc) * (kTileRows * kKChunk * 2);
+    w_out = *reinterpret_cast<const uint4*>(w + wt_lane);
     word_out = (xpart ? sgx : sgh)[static_cast<int64_t>(cc) * (4 * H)];
   };
   // Selects the probe's weights for row ra of one chunk (8 bf16 weights wv and the row's sign
@@ -273,9 +299,8 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   };
 
   // One K step on chunk c (c % 4 == S). Requests go out at the top: on odd steps the weights of
-  // chunks c+5 and c+6 (the two 64-byte halves of each row's 128-byte line, back to back, so that
-  // the L1 fetches every line once), then in every step the activations of chunk c+3 (one chunk
-  // per step keeps the request stream even). Vector loads complete in issue order, and each
+  // chunks c+5 and c+6, then in every step the activations of chunk c+3 (one chunk per step
+  // keeps the request stream even). Vector loads complete in issue order, and each
   // stream is consumed in issue order, so this order never makes a wait for one chunk hold up a
   // newer chunk: the weights of chunk c+5 are waited for in step c+1, after everything issued
   // before them was needed anyway. Row groups 0-5 are multiplied, each followed
