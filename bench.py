@@ -11,9 +11,10 @@ rollsum, which score only the output part of each sequence).
 
 Printed JSON line:
   value        perturbed-forward tokens per second over whole steps, 2K * B * T / step time
-  roofline     the recurrent gate kernel (the dominant kernel): algorithmic matrix-core flops
-               per launch / mean launch duration from HIP events on the launch stream, against
-               the bf16 dense MFMA peak
+  roofline     the recurrent gate kernel (the dominant kernel, named by the library): algorithmic
+               flops per launch / mean launch duration from HIP events on the launch stream,
+               against the bf16 dense MFMA peak, or the 157.3 TFLOP/s fp32 peak (matrix cores for
+               k_lstm_f32_sliced, vector ALUs for k_lstm_f32)
   update_roofline  the update kernel against HBM (algorithmic bytes / launch time), with its
                ALU issue floor next to it
   cpu_baseline the plain single-threaded CPU oracle on a bounded sample of the same workload: on
@@ -360,8 +361,15 @@ def main():
     gate_flops_per_launch = work[0] / max(gate_n, 1)
     gate_mean_s = gate_ms / 1e3 / max(gate_n, 1)
     achieved = gate_flops_per_launch / gate_mean_s / 1e12 if gate_n else 0.0
+    gate_kernel = b.cdrge_timed_kernel(ctx.ctx, 0)
+    upd_kernel = b.cdrge_timed_kernel(ctx.ctx, 2)
     peak = PEAK["bf16_mfma_tflops"] if bf16 else PEAK["fp32_tflops"]
-    traffic = traffic_from_profiles("gates_bf16" if bf16 else "lstm_f32", args.workload)
+    # the row-sliced fp32 kernel multiplies W on the fp32 matrix cores (157.3 TFLOP/s dense); the
+    # persistent one on the vector ALUs (157.3 TFLOP/s with packed FMAs)
+    gate_bound = "mfma" if bf16 or gate_kernel == "k_lstm_f32_sliced" else "alu"
+    traffic = traffic_from_profiles({"k_lstm_gates_bf16": "gates_bf16", "k_lstm_f32": "lstm_f32",
+                                     "k_lstm_f32_sliced": "lstm_f32_sliced"}.get(gate_kernel, gate_kernel),
+                                    args.workload)
     upd_traffic = traffic_from_profiles("update_bf16" if bf16 else "update_f32", args.workload)
     upd_ms, upd_n = timing[2]
     upd_gbs = work[2] / (upd_ms / 1e3) / 1e9 if upd_n else 0.0
@@ -392,13 +400,11 @@ def main():
         "ms_per_timestep": step_s * 1e3 / p.seq_len,
         "workspace_bytes": b.cdrge_workspace_bytes(cfg),
         "forward_only_tokens_per_sec": tokens_per_step / fwd_s,
-        "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": "k_lstm_gates_bf16"
-                     if bf16 else "k_lstm_f32",
+        "roofline": {"bound": gate_bound, "kernel": gate_kernel,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "launches": gate_n, "mean_launch_ms": gate_mean_s * 1e3,
                      "flops_per_launch": gate_flops_per_launch},
-        "update_roofline": {"bound": "hbm", "kernel": "k_update_perm" if bf16 and p.n_probes <= 64
-                            else "k_update_lut", "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+        "update_roofline": {"bound": "hbm", "kernel": upd_kernel, "achieved": upd_gbs, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
                             "frac": upd_gbs / PEAK["hbm_gbs"], "traffic": upd_traffic, "launches": upd_n,
                             "total_ms_per_step": upd_ms / args.steps,
                             "alu": update_alu_floor(args.workload, upd_ms / max(upd_n, 1))},

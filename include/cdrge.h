@@ -185,6 +185,12 @@ cdrge_status cdrge_get_timing(cdrge_ctx* ctx, int kind, double* total_ms, int64_
  * for kind 2. */
 cdrge_status cdrge_get_work(cdrge_ctx* ctx, int kind, double* work);
 
+/* Name of the kernel whose launches are timed under `kind` for this context's configuration
+ * (kind 0: k_lstm_gates_bf16, k_lstm_f32 or k_lstm_f32_sliced; 1: k_logits_ce_bf16,
+ * k_ce_f32_sliced, or "" when the persistent fp32 kernel computes the loss itself; 2: the update
+ * kernel; 3 and invalid arguments: ""). Static storage, never freed. */
+const char* cdrge_timed_kernel(const cdrge_ctx* ctx, int kind);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): one whole step, as cdrge_step, with no context and no
  * caller workspace. The workspace lives in a static device array of the library, one per device

@@ -37,6 +37,14 @@ SMALL = {
     "f32_min": b.make_config(1, 2, 1, 1, 1, 1, 1, "f32", 1e-2, 1e-2, 86),
     # a long sequence: 64 steps through the same fixed-size state
     "bf16_long": b.make_config(2, 50, 64, 128, 24, 64, 2, "bf16", 1e-4, 1e-4, 87),
+    # fp32 on the row-sliced kernels (E and H multiples of 32, V <= 64, B >= 8, >= 256 columns per
+    # chunk): 320 columns (five whole 64-column blocks), two layers of four row slices
+    "f32sl_b8": b.make_config(2, 11, 32, 64, 8, 4, 20, "f32", 1e-3, 1e-3, 88),
+    # nine sequences per model (pairs straddle the 64-column blocks), chunks of 15 and 10 pairs
+    # (270 and 180 columns, ragged blocks), two row slices
+    "f32sl_b9_chunks": b.make_config(1, 40, 64, 32, 9, 3, 25, "f32", 1e-3, 1e-3, 89, probes_per_chunk=15),
+    # three layers, six row slices, the largest vocabulary of the sliced path
+    "f32sl_v64": b.make_config(3, 64, 32, 96, 10, 2, 15, "f32", 1e-3, 1e-3, 90),
 }
 
 
@@ -58,6 +66,11 @@ def test_small_step_parity(oracle, name):
     theta, tokens = _inputs(c, 5)
     tol = TOL[dtype_name(c)]
     run = HipRun(c, theta, tokens)
+    # the cases cover both fp32 kernels: the f32sl_ ones the row-sliced path, the others the
+    # persistent one
+    expect = ("k_lstm_f32_sliced" if name.startswith("f32sl") else "k_lstm_f32") if c.dtype == b.CDRGE_F32 \
+        else "k_lstm_gates_bf16"
+    assert b.cdrge_timed_kernel(run.ctx.ctx, 0) == expect
     losses, seq, st = run.probe_losses(step=2)
     assert st == 0
     oc = ocfg(c)
@@ -316,6 +329,11 @@ def test_probe_dominant_bf16(oracle, name):
     theta32, tokens = probe_case_inputs(PROBE_CASES[name])
     theta = to_bf16_bits(theta32)
     run = HipRun(c, theta, tokens)
+    # the cases cover both fp32 kernels: the f32sl_ ones the row-sliced path, the others the
+    # persistent one
+    expect = ("k_lstm_f32_sliced" if name.startswith("f32sl") else "k_lstm_f32") if c.dtype == b.CDRGE_F32 \
+        else "k_lstm_gates_bf16"
+    assert b.cdrge_timed_kernel(run.ctx.ctx, 0) == expect
     losses, seq, st = run.probe_losses(step=2)
     assert st == 0
     oc = ocfg(c)

@@ -67,6 +67,7 @@ EXPORTS = {
     "cdrge_get_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int]),
     "cdrge_get_work": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
+    "cdrge_timed_kernel": (ctypes.c_char_p, [ctypes.c_void_p, ctypes.c_int]),
     "cdrge_probe_losses_io": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                              ctypes.c_void_p, ctypes.c_void_p]),
     "cdrge_step_io": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
@@ -196,6 +197,10 @@ def cdrge_get_work(ctx, kind: int) -> float:
     w = ctypes.c_double()
     _check(lib().cdrge_get_work(ctx, kind, ctypes.byref(w)), "cdrge_get_work")
     return w.value
+
+
+def cdrge_timed_kernel(ctx, kind: int) -> str:
+    return lib().cdrge_timed_kernel(ctx, kind).decode()
 
 
 def cdrge_step_noalloc(cfg: cdrge_config, params, tokens, step: int, losses, stream=None):

@@ -335,4 +335,19 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(
   }
 }
 
+// LSTM cell from the four gate pre-activations: sigmoid(x) = 1 / (1 + e^-x),
+// tanh(x) = 2 / (1 + e^-2x) - 1, c' = sigmoid(f) c + sigmoid(i) tanh(g), h = sigmoid(o) tanh(c').
+// Written this way the functions saturate correctly without clamping (e^-x = inf gives 0 and
+// -1) and a NaN argument stays NaN; each cell costs 5 exponentials and 5 reciprocals.
+__device__ __forceinline__ float cell_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float cell_tanh(float x) {
+  return 2.f * __builtin_amdgcn_rcpf(1.f + __expf(-2.f * x)) - 1.f;
+}
+__device__ __forceinline__ void lstm_cell(float gi, float gf, float gg, float go, float c, float& c_out,
+                                          float& h_out) {
+  const float cn = cell_sigmoid(gf) * c + cell_sigmoid(gi) * cell_tanh(gg);
+  c_out = cn;
+  h_out = cell_sigmoid(go) * cell_tanh(cn);
+}
+
 }  // namespace cdrge
