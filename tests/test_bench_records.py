@@ -54,7 +54,10 @@ def test_record_contract(path):
         # algorithmic flops per launch / mean launch duration
         assert r["achieved"] == pytest.approx(r["flops_per_launch"] / (r["mean_launch_ms"] / 1e3) / 1e12, rel=1e-9)
     else:
-        assert (r["bound"], r["unit"], r["peak"]) == ("alu", "TFLOP/s", 157.3)
+        # fp32: the row-sliced kernel on the fp32 matrix cores, the persistent one on the vector ALUs
+        bound = "mfma" if r["kernel"] == "k_lstm_f32_sliced" else "alu"
+        assert r["kernel"] in ("k_lstm_f32", "k_lstm_f32_sliced")
+        assert (r["bound"], r["unit"], r["peak"]) == (bound, "TFLOP/s", 157.3)
     assert r["traffic"] is None or r["traffic"] > 0
     cb = d["cpu_baseline"]
     assert CPU_KEYS <= set(cb) and cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
