@@ -154,7 +154,7 @@ __device__ __forceinline__ void f32_column(float (&acc)[2 * G * NB], float w, co
 }
 
 // Tables of signed partial sums of x ([K][M] in LDS) for the nibbles of the sign words:
-// tab[((w * 8 + j) * M + s) * 16 + m] = sum over i < 4 of (bit i of m ? -x : x)[col_i][s], where
+// tab[((w * 8 + j) * 16 + m) * M + s] = sum over i < 4 of (bit i of m ? -x : x)[col_i][s], where
 // col_i is the column of bit position 4 j + i of word w (2 (p & 15) + (p >> 4) for p = 4 j + i);
 // columns at or past K count as zero.
 template <int M>
@@ -172,9 +172,11 @@ __device__ __forceinline__ void f32_build_tables(const float* x, int K, float* t
     // bits 0, 1 of m select the signs of v0, v1; bits 2, 3 those of v2, v3
     const float lo[4] = {v[0] + v[1], v[1] - v[0], v[0] - v[1], -v[0] - v[1]};
     const float hi[4] = {v[2] + v[3], v[3] - v[2], v[2] - v[3], -v[2] - v[3]};
-    float4* dst = reinterpret_cast<float4*>(tab + static_cast<int64_t>(i) * 16);
+    // the slots of one nibble value are contiguous, so that the 2 NB slots of a pair (which share
+    // the pair's sign word) are read together
+    float* dst = tab + static_cast<int64_t>(wj) * 16 * M + sl;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = make_float4(lo[0] + hi[q], lo[1] + hi[q], lo[2] + hi[q], lo[3] + hi[q]);
+    for (int m = 0; m < 16; ++m) dst[m * M] = lo[m & 3] + hi[m >> 2];
   }
 }
 
@@ -193,18 +195,25 @@ __device__ __forceinline__ void f32_row_dot_split(float (&accw)[2 * G * NB], flo
 #pragma unroll
     for (int g = 0; g < G; ++g) word[g] = (sg + (static_cast<int64_t>(qg[g]) * nw + kw) * ld)[r];
     const int k0 = 32 * kw;
-    auto column = [&](int k) {
-      const float w = (wt + static_cast<int64_t>(k) * ld)[r];
+    // W^T column k is a wave-uniform base (advanced by one row of W^T per column) plus this
+    // lane's 32-bit byte offset; the activations of the 32 columns are at fixed offsets from xk
+    const char* wcol = reinterpret_cast<const char*>(wt + static_cast<int64_t>(k0) * ld);
+    const size_t wstep = sizeof(float) * static_cast<size_t>(ld);
+    const uint32_t roff = static_cast<uint32_t>(r) * 4u;
+    const float* xk = x + k0 * M;
+    auto column = [&](int kk) {
+      const float w = *reinterpret_cast<const float*>(wcol + roff);
+      wcol += wstep;
       float xv[M];
-      f32_load_slots<M>(x + k * M, xv);
+      f32_load_slots<M>(xk + kk * M, xv);
 #pragma unroll
       for (int i = 0; i < M; ++i) accw[i] = fmaf(w, xv[i], accw[i]);
     };
     if (k0 + 32 <= K) {
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) column(k0 + kk);
+      for (int kk = 0; kk < 32; ++kk) column(kk);
     } else {
-      for (int k = k0; k < K; ++k) column(k);
+      for (int kk = 0; kk < K - k0; ++kk) column(kk);
     }
     const float* tw = tab + kw * 8 * M * 16;
 #pragma unroll
@@ -212,8 +221,10 @@ __device__ __forceinline__ void f32_row_dot_split(float (&accw)[2 * G * NB], flo
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const uint32_t nib = (word[g] >> (4 * j)) & 15u;
+        float tv[2 * NB];
+        f32_load_slots<2 * NB>(tw + (j * 16 + nib) * M + 2 * g * NB, tv);
 #pragma unroll
-        for (int i = 2 * g * NB; i < 2 * (g + 1) * NB; ++i) accp[i] += tw[(j * M + i) * 16 + nib];
+        for (int i = 0; i < 2 * NB; ++i) accp[2 * g * NB + i] += tv[i];
       }
     }
   }
@@ -344,12 +355,14 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
 #pragma unroll
       for (int i = 0; i < M; ++i) acc[i] = 0.f;
       uint32_t word[G];
+      const float* wo = a.wt_out + static_cast<int64_t>(k0) * V + v;  // W_out^T column k, row v
       for (int k = k0; k < k1; ++k) {
         if (k == k0 || (k & 31) == 0) {
 #pragma unroll
           for (int g = 0; g < G; ++g) word[g] = (a.sg_out + (static_cast<int64_t>(qg[g]) * nw + (k >> 5)) * V)[v];
         }
-        const float w = (a.wt_out + static_cast<int64_t>(k) * V)[v];
+        const float w = *wo;
+        wo += V;
         f32_column<G, NB>(acc, w, hl + k * M, word, sign_bit_pos(static_cast<uint32_t>(k)), a.eps);
       }
       f32_store_slots<M>(gbuf + (j * V + v) * M, acc);
