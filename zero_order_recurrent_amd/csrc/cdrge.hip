@@ -110,7 +110,8 @@ int64_t param_count(const cdrge_config* c) {
 // faster: 3.55 against 5.44 ms per step at 1,024 models, H = 256, T = 100.
 bool f32_sliced_ok(const cdrge_config* c, int P) {
   return c->dtype == CDRGE_F32 && c->embed % 32 == 0 && c->hidden % 32 == 0 && c->vocab <= kSlMaxV &&
-         c->batch >= 8 && int64_t(2) * P * c->batch >= 256 && c->n_layers <= kF32MaxLayers;
+         c->batch >= 8 && int64_t(2) * P * c->batch >= 256 && int64_t(2) * P * c->batch < (int64_t(1) << 30) &&
+         c->n_layers <= kF32MaxLayers;
 }
 
 cdrge_status supported(const cdrge_config* c) {
