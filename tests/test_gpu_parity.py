@@ -45,6 +45,9 @@ SMALL = {
     "f32sl_b9_chunks": b.make_config(1, 40, 64, 32, 9, 3, 25, "f32", 1e-3, 1e-3, 89, probes_per_chunk=15),
     # three layers, six row slices, the largest vocabulary of the sliced path
     "f32sl_v64": b.make_config(3, 64, 32, 96, 10, 2, 15, "f32", 1e-3, 1e-3, 90),
+    # char-LM widths in fp32 (E = 128, H = 1,024): per-model state beyond the persistent kernel's
+    # LDS, so only the row-sliced kernels run it (64 row slices, four 64-column blocks)
+    "f32sl_h1024": b.make_config(1, 50, 128, 1024, 16, 3, 8, "f32", 1e-3, 1e-3, 91),
 }
 
 
