@@ -102,7 +102,7 @@ def _oracle_config(preset):
 
 
 def cpu_worker(args) -> None:
-    """Child process of the all-cores leg: one probe pair (both signs) over its own sequences."""
+    """Child process of the all-cores leg: its probe pairs (both signs) over its own sequences."""
     from oracle import Oracle
     from zero_order_recurrent_amd.inputs import PRESETS
     theta = np.load(os.path.join(args.cpu_worker, "theta.npy"), mmap_mode="r")
@@ -111,19 +111,23 @@ def cpu_worker(args) -> None:
     p = PRESETS[args.workload].with_(seq_len=inputs.shape[1])
     o = Oracle()
     seqs = [int(v) for v in args.worker_seqs.split(",")]
+    probes = [int(v) for v in args.worker_probe.split(",")]
     # everything is loaded: wait for the parent's start signal, so that all workers run together
     print("ready", flush=True)
     sys.stdin.readline()
     t0 = time.perf_counter()
-    o.probe_losses_io(_oracle_config(p), theta, inputs, targets, 0, probe_ids=[args.worker_probe], seq_ids=seqs)
+    o.probe_losses_io(_oracle_config(p), theta, inputs, targets, 0, probe_ids=probes, seq_ids=seqs)
     dt = time.perf_counter() - t0
-    print(json.dumps({"seconds": dt, "tokens": 2 * len(seqs) * p.seq_len}), flush=True)
+    print(json.dumps({"seconds": dt, "tokens": 2 * len(probes) * len(seqs) * p.seq_len}), flush=True)
 
 
 def cpu_baseline(preset, theta, inputs, targets, budget_s: float) -> dict:
     """The oracle (plain single-threaded C++) on the host's cores, on a bounded sample of the
     workload: one probe pair, both signs, over full sequences, at full model shape, including the
-    perturbed parameter copies the oracle builds for each sign.
+    perturbed parameter copies the oracle builds for each sign. When the extrapolated whole step
+    fits three times the budget (the small fp32 workloads), the whole step is run and measured
+    instead. The reported value is the faster of the two legs (for tiny models the processes of the
+    all-cores leg cost more than the work they share).
 
     1 core: the copies alone (0 sequences) and then with n sequences give the fixed cost per
     perturbed model and the cost per sequence; with the oracle's update timed on a slice of
@@ -169,12 +173,33 @@ def cpu_baseline(preset, theta, inputs, targets, budget_s: float) -> dict:
                                f"{models} x {preset.batch} sequences x {per_seq:.3g} s + update "
                                f"{t_upd:.3g} s (timed on {n_upd} of {d} parameters)")
 
+    # When the whole step fits the budget (the small fp32 workloads), it is measured rather than
+    # extrapolated: every probe pair over every sequence, then the full update.
+    full = step_1core <= 3 * budget_s
+    if full:
+        t0 = time.perf_counter()
+        full_l, _ = o.probe_losses_io(oc, theta, inputs, targets, 0)
+        t_fwd = time.perf_counter() - t0
+        work = theta.copy()
+        t0 = time.perf_counter()
+        o.update(oc, work, 0, full_l)
+        t_up = time.perf_counter() - t0
+        del work
+        single = {"value": models * preset.batch * preset.seq_len / t_fwd, "cores": 1, "seconds": t_fwd,
+                  "sample": f"the whole step: all {preset.n_probes} probe pairs (both signs) x {preset.batch} "
+                            f"sequence(s) x T={preset.seq_len}, then the update",
+                  "full_step_s": t_fwd + t_up, "extrapolated_full_step_s": t_fwd + t_up,
+                  "extrapolation": "measured, not extrapolated"}
+        step_1core = t_fwd + t_up
+
     # all cores: disjoint (probe pair, sequences) slices in child processes
     info = cpu_info()
     per_proc_bytes = 4 * d + (256 << 20)
     mem_cap = max(1, int(0.6 * _mem_available() // per_proc_bytes)) if _mem_available() else 1
     workers = max(1, min(info["nproc"], 16, mem_cap, preset.n_probes * preset.batch))
     n_each = max(1, min(n_seq, preset.batch * preset.n_probes // workers))
+    if full:  # every worker: its share of the probe pairs over all sequences
+        workers = max(1, min(workers, preset.n_probes))
     allcores = None
     if workers > 1:
         tmp = tempfile.mkdtemp(prefix="cdrge_cpu_")
@@ -184,12 +209,16 @@ def cpu_baseline(preset, theta, inputs, targets, budget_s: float) -> dict:
             np.save(os.path.join(tmp, "targets.npy"), targets)
             procs = []
             for w in range(workers):
-                probe = w % preset.n_probes
-                first = (w // preset.n_probes) * n_each
-                seqs = ",".join(str((first + q) % preset.batch) for q in range(n_each))
+                if full:
+                    probes = ",".join(str(q) for q in range(w, preset.n_probes, workers))
+                    seqs = ",".join(str(q) for q in range(preset.batch))
+                else:
+                    probes = str(w % preset.n_probes)
+                    first = (w // preset.n_probes) * n_each
+                    seqs = ",".join(str((first + q) % preset.batch) for q in range(n_each))
                 procs.append(subprocess.Popen(
                     [sys.executable, os.path.abspath(__file__), "--workload", preset.name, "--cpu-worker", tmp,
-                     "--worker-probe", str(probe), "--worker-seqs", seqs],
+                     "--worker-probe", probes, "--worker-seqs", seqs],
                     stdin=subprocess.PIPE, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
             for pr in procs:  # every worker has its inputs loaded
                 if pr.stdout.readline().strip() != "ready":
@@ -214,14 +243,22 @@ def cpu_baseline(preset, theta, inputs, targets, budget_s: float) -> dict:
             os.rmdir(tmp)
         toks = sum(r["tokens"] for r in outs)
         speedup = (toks / wall) / single["value"]
-        allcores = {"value": toks / wall, "cores": workers, "seconds": wall,
-                    "sample": f"{workers} oracle processes, each one probe pair (both signs) x {n_each} "
-                              f"sequence(s) x T={preset.seq_len} at full model shape with its own perturbed "
-                              f"copies; disjoint (probe, sequence) slices",
-                    "extrapolated_full_step_s": step_1core / speedup,
-                    "extrapolation": f"extrapolated, not measured: the 1-core step divided by the measured "
-                                     f"speed-up of {speedup:.2f} on {workers} processes"}
-    best = allcores if allcores is not None else single
+        if full:
+            allcores = {"value": toks / wall, "cores": workers, "seconds": wall,
+                        "sample": f"{workers} oracle processes sharing all {preset.n_probes} probe pairs (both "
+                                  f"signs) x {preset.batch} sequence(s) x T={preset.seq_len}: the whole forward "
+                                  f"of the step",
+                        "extrapolated_full_step_s": wall + (step_1core - single["seconds"]),
+                        "extrapolation": "the forward measured on all processes, plus the 1-core update"}
+        else:
+            allcores = {"value": toks / wall, "cores": workers, "seconds": wall,
+                        "sample": f"{workers} oracle processes, each one probe pair (both signs) x {n_each} "
+                                  f"sequence(s) x T={preset.seq_len} at full model shape with its own perturbed "
+                                  f"copies; disjoint (probe, sequence) slices",
+                        "extrapolated_full_step_s": step_1core / speedup,
+                        "extrapolation": f"extrapolated, not measured: the 1-core step divided by the measured "
+                                         f"speed-up of {speedup:.2f} on {workers} processes"}
+    best = allcores if allcores is not None and allcores["value"] > single["value"] else single
     out = {"value": best["value"], "unit": "perturbed-forward tokens/s", "cores": best["cores"], "kind": "oracle",
            "sample": best["sample"] + f"; {best['seconds']:.1f} s",
            "extrapolated_full_step_s": best["extrapolated_full_step_s"],
@@ -263,7 +300,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
-    ap.add_argument("--worker-probe", type=int, default=0, help=argparse.SUPPRESS)
+    ap.add_argument("--worker-probe", default="0", help=argparse.SUPPRESS)
     ap.add_argument("--worker-seqs", default="0", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_worker:
