@@ -48,6 +48,8 @@ SMALL = {
     # char-LM widths in fp32 (E = 128, H = 1,024): per-model state beyond the persistent kernel's
     # LDS, so only the row-sliced kernels run it (64 row slices, four 64-column blocks)
     "f32sl_h1024": b.make_config(1, 50, 128, 1024, 16, 3, 8, "f32", 1e-3, 1e-3, 91),
+    # one timestep: only the first (no W_hh, zero state) launch and one cross-entropy
+    "f32sl_t1": b.make_config(2, 20, 64, 64, 8, 1, 16, "f32", 1e-3, 1e-3, 92),
 }
 
 

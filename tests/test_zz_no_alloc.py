@@ -19,6 +19,9 @@ PAIRS = {
     # fp32: the tiny workload's shape, then a smaller model
     "f32": (b.make_config(1, 16, 16, 32, 4, 10, 8, "f32", 1e-3, 1e-3, 503),
             b.make_config(1, 7, 12, 8, 3, 4, 5, "f32", 1e-3, 1e-3, 504)),
+    # fp32 on the row-sliced kernels: two layers over 320 columns, then one layer over 256
+    "f32_sliced": (b.make_config(2, 10, 32, 64, 8, 5, 20, "f32", 1e-3, 1e-3, 505),
+                   b.make_config(1, 10, 32, 32, 16, 3, 8, "f32", 1e-3, 1e-3, 506)),
 }
 
 
@@ -33,8 +36,10 @@ def _inputs(c, seed):
     return theta, tokens
 
 
-def _with_context(c, theta, tokens, step):
+def _with_context(c, theta, tokens, step, kernel=None):
     run = HipRun(c, theta, tokens)
+    if kernel is not None:
+        assert b.cdrge_timed_kernel(run.ctx.ctx, 0) == kernel
     losses = run.ctx.step(run.tokens, step).cpu().numpy().copy()
     assert run.ctx.sync_status() == 0
     out = run.theta()
@@ -57,7 +62,8 @@ def test_noalloc_step_matches_context_step(dtype):
     for k, c in enumerate(PAIRS[dtype]):
         say(f"[gpu] no-alloc step {dtype}, call {k + 1}")
         theta, tokens = _inputs(c, 40 + k)
-        ref_l, ref_t = _with_context(c, theta, tokens, step=3)
+        ref_l, ref_t = _with_context(c, theta, tokens, step=3,
+                                     kernel="k_lstm_f32_sliced" if dtype == "f32_sliced" else None)
         got_l, got_t = _noalloc(c, theta, tokens, step=3)
         assert np.isfinite(ref_l).all()
         np.testing.assert_array_equal(got_l, ref_l)
