@@ -14,10 +14,11 @@
 //   * W [x; h] is shared by all models: v_mfma_f32_16x16x4_f32 on fp32 operands staged in LDS;
 //   * P [x; h] differs per pair: for every column and group of 4 K-columns that one nibble of a
 //     sign word covers, the 16 signed sums +-x_a +-x_b +-x_c +-x_d are tabulated in LDS once per
-//     32-wide K chunk, and each (row, column) adds the entry its nibble selects. The table's
-//     address is built by one byte permute: the nibble lands in address byte 1 (entries of one
-//     nibble value are one 256-byte row of 64 columns) and the column in byte 0, so the tables
-//     start at LDS address 0 (the kernel has no static LDS).
+//     32-wide K chunk, and each (row, column) adds the entry its nibble selects. Two adjacent
+//     columns always belong to one probe pair and share the nibble, so one 8-byte read serves
+//     both. The read's address is built by one byte permute: the nibble lands in address byte 1
+//     (entries of one nibble value are one 256-byte row of 64 columns) and the column pair in
+//     byte 0, so the tables start at LDS address 0 (the kernel has no static LDS).
 // The perturbed biases come from a per-chunk table. The four gates of a hidden unit meet in one
 // lane of the matrix-core output (local row 4u + g is gate g of unit u), so the LSTM cell runs in
 // registers; c and h live in global memory as [H][columns], h ping-ponged per layer.
@@ -52,8 +53,9 @@ constexpr int kSlLdsBytes = kSlSOff + 2 * kSlMaxPairs * kSlRows * 4;  // 80 KB: 
 constexpr int kSlHsOff = kSlRows * kSlPStride * 4;                  // h [16][64] after the exchange buffer
 
 typedef float f32x4_sl __attribute__((ext_vector_type(4)));
-// A float in LDS by its byte address: the kernel has no static LDS, so its dynamic LDS (and the
-// sign-sum tables at its start) begins at address 0; the host checks that before using the kernel.
+// Two floats in LDS by their byte address: the kernel has no static LDS, so its dynamic LDS (and
+// the sign-sum tables at its start) begins at address 0; the host checks that before using the
+// kernel.
 typedef float f32x2_sl __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) const f32x2_sl SlLdsFloat2;
 
