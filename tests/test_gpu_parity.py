@@ -50,6 +50,11 @@ SMALL = {
     "f32sl_h1024": b.make_config(1, 50, 128, 1024, 16, 3, 8, "f32", 1e-3, 1e-3, 91),
     # one timestep: only the first (no W_hh, zero state) launch and one cross-entropy
     "f32sl_t1": b.make_config(2, 20, 64, 64, 8, 1, 16, "f32", 1e-3, 1e-3, 92),
+    # B a multiple of 16: the direct variant (perturbed weights as the matrix-core operand), two
+    # layers, chunks of 10 and 5 pairs (320 and 160 columns)
+    "f32sl_direct_chunks": b.make_config(2, 11, 32, 64, 16, 4, 15, "f32", 1e-3, 1e-3, 93, probes_per_chunk=10),
+    # the direct variant with 32 sequences per model (two models per 64-column block), V = 64
+    "f32sl_direct_b32": b.make_config(1, 64, 64, 96, 32, 3, 5, "f32", 1e-3, 1e-3, 94),
 }
 
 

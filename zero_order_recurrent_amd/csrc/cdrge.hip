@@ -389,7 +389,10 @@ cdrge_status enqueue_f32_sliced(cdrge_ctx* ctx, const TokenRefs& tr, int pair0, 
       const double flops = 2.0 * 4 * p.H * (double(tih.cols) + (t > 0 ? p.H : 0)) * ncols +
                            (l == p.L - 1 ? 2.0 * p.V * p.H * ncols : 0.0);
       CDRGE_TRY(timed(ctx, 0, flops, [&] {
-        hipLaunchKernelGGL(k_lstm_f32_sliced, grid, dim3(kSlThreads), kSlLdsBytes, s, g);
+        if (p.B % 16 == 0)
+          hipLaunchKernelGGL(k_lstm_f32_sliced<true>, grid, dim3(kSlThreads), kSlDirLdsBytes, s, g);
+        else
+          hipLaunchKernelGGL(k_lstm_f32_sliced<false>, grid, dim3(kSlThreads), kSlLdsBytes, s, g);
       }));
     }
     CDRGE_TRY(timed(ctx, 1, 0.0, [&] {
@@ -799,12 +802,16 @@ cdrge_status init_device(cdrge_ctx* ctx, const cdrge_config* cfg) {
   } else {
     const Plan& p = ctx->plan;
     if (p.f32_sliced) {
-      // its sign-sum tables are addressed from LDS address 0: no static LDS allowed
-      const void* f = reinterpret_cast<const void*>(k_lstm_f32_sliced);
+      // with B a multiple of 16 the direct variant (no tables); otherwise the one whose sign-sum
+      // tables are addressed from LDS address 0, which needs a kernel without static LDS
+      const bool direct = p.B % 16 == 0;
+      const void* f = direct ? reinterpret_cast<const void*>(k_lstm_f32_sliced<true>)
+                             : reinterpret_cast<const void*>(k_lstm_f32_sliced<false>);
       hipFuncAttributes fa{};
       CDRGE_HIP(hipFuncGetAttributes(&fa, f));
       if (fa.sharedSizeBytes != 0) return device_error("k_lstm_f32_sliced has static LDS", hipErrorInvalidValue);
-      CDRGE_HIP(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSlLdsBytes));
+      CDRGE_HIP(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    direct ? kSlDirLdsBytes : kSlLdsBytes));
     } else {
       const int lds = static_cast<int>(
           sizeof(float) * f32_lds_layout(p.L, p.V, p.E, p.H, p.f32_g, p.f32_nb, p.f32_threads).total);

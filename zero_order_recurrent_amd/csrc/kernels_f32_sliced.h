@@ -51,6 +51,10 @@ constexpr int kSlXOff = kSlWOff + 2 * 32 * kSlRows * 4;             // activatio
 constexpr int kSlSOff = kSlXOff + 2 * 32 * kSlCols * 4;             // sign words [2][32 pairs][64 rows]
 constexpr int kSlLdsBytes = kSlSOff + 2 * kSlMaxPairs * kSlRows * 4;  // 80 KB: two workgroups per CU
 constexpr int kSlHsOff = kSlRows * kSlPStride * 4;                  // h [16][64] after the exchange buffer
+// The direct variant (B a multiple of 16) has no tables: h [16][64] at 0, then W^T, activations
+// and sign words as above, 52 KB in all (three workgroups per CU).
+constexpr int kSlDirBase = 4096;
+constexpr int kSlDirLdsBytes = kSlDirBase + (kSlLdsBytes - kSlWOff);
 
 typedef float f32x4_sl __attribute__((ext_vector_type(4)));
 // Two floats in LDS by their byte address: the kernel has no static LDS, so its dynamic LDS (and
@@ -78,12 +82,24 @@ struct F32SlArgs {
   int in, H, B, V, L, layer, t, ncols, ncp, pc, in_stride, first, last;
 };
 
-// grid (H / 16, ncp / 64), block 256, dynamic LDS kSlLdsBytes. Requires in % 32 == 0,
-// H % 32 == 0, V <= kSlMaxV. Column s = m B + b is sequence b of model m (model 2q + side of pair
-// q); columns at or past ncols are computed from whatever the padding holds and not written.
-__global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) {
+// grid (H / 16, ncp / 64), block 256, dynamic LDS kSlLdsBytes (kDirect: kSlDirLdsBytes). Requires
+// in % 32 == 0, H % 32 == 0, V <= kSlMaxV, and for kDirect B % 16 == 0. Column s = m B + b is
+// sequence b of model m (model 2q + side of pair q); columns at or past ncols are computed from
+// whatever the padding holds and not written.
+//
+// kDirect: when B is a multiple of 16, every 16-column matrix-core tile lies in one model, so the
+// perturbed weight itself can be the A operand: each lane forms fl(w +- eps p) for its element of
+// the tile's model (R-8's perturbed weight, rounded once in fp32) and the matrix cores multiply it
+// with the activations. No sign-sum tables, no P x exchange, one barrier per K chunk.
+template <bool kDirect>
+__global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced(F32SlArgs a) {
   extern __shared__ __align__(16) float sl_lds[];
   char* const lds = reinterpret_cast<char*>(sl_lds);
+  // LDS offsets of the staged chunk (the direct variant has no tables in front of them)
+  constexpr int kWOff = kDirect ? kSlDirBase : kSlWOff;
+  constexpr int kXOff = kWOff + (kSlXOff - kSlWOff);
+  constexpr int kSOff = kWOff + (kSlSOff - kSlWOff);
+  constexpr int kHsOff = kDirect ? 0 : kSlHsOff;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, G4 = 4 * H;
@@ -156,9 +172,9 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
     }
   };
   auto lstore = [&](int kc, int buf, const Regs& rg) {
-    float* wk = reinterpret_cast<float*>(lds + kSlWOff) + buf * 32 * kSlRows;
-    float* xk = reinterpret_cast<float*>(lds + kSlXOff) + buf * 32 * kSlCols;
-    uint32_t* sk = reinterpret_cast<uint32_t*>(lds + kSlSOff) + buf * kSlMaxPairs * kSlRows;
+    float* wk = reinterpret_cast<float*>(lds + kWOff) + buf * 32 * kSlRows;
+    float* xk = reinterpret_cast<float*>(lds + kXOff) + buf * 32 * kSlCols;
+    uint32_t* sk = reinterpret_cast<uint32_t*>(lds + kSOff) + buf * kSlMaxPairs * kSlRows;
 #pragma unroll
     for (int i = 0; i < 8; ++i) wk[tid + 256 * i] = rg.w[i];
     if (kc < kx && emb_in) {
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
   // and 2 (tid >> 6) + 1). Bit position p of a sign word is column 2 (p & 15) + (p >> 4) of the
   // chunk; entry v of nibble j is the sum over i < 4 of (bit i of v ? -x : x) at bit 4 j + i.
   auto build = [&](int buf) {
-    const float* xk = reinterpret_cast<const float*>(lds + kSlXOff) + buf * 32 * kSlCols;
+    const float* xk = reinterpret_cast<const float*>(lds + kXOff) + buf * 32 * kSlCols;
     float* tab = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -207,8 +223,18 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4_sl{0.f, 0.f, 0.f, 0.f};
   const int fi = lane & 15, fk = lane >> 4;
-  const int a_off = fk * kSlRows + (fi & 3) * 16 + 4 * wave + (fi >> 2);
+  const int a_pos = (fi & 3) * 16 + 4 * wave + (fi >> 2);  // position p of the lane's A row
+  const int a_off = fk * kSlRows + a_pos;
   const int b_off = fk * kSlCols + fi;
+  // direct variant: the model of each 16-column tile, its pair within the block and its signed eps
+  int tile_qi[4];
+  float tile_e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = min(min(s0 + 16 * j, a.ncols - 1) / a.B, 2 * a.pc - 1);
+    tile_qi[j] = min((m >> 1) - q_first, kSlMaxPairs - 1);
+    tile_e[j] = (m & 1) ? -a.eps : a.eps;
+  }
   // ---- sign-sum role: thread (column pair cp = tid & 31, row group rg = tid >> 5) owns columns
   // 2 cp, 2 cp + 1 and positions p = 8 rg + i. Columns 2k and 2k + 1 always belong to one probe
   // pair (a pair's 2B columns start at a multiple of 2B), so they share the nibble and one 8-byte
@@ -224,14 +250,41 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
   // Chunk kc + 1 is requested at the top of step kc and written to LDS buffer (kc + 1) & 1 at its
   // end.
   Regs rg;
+  // the direct variant requests two chunks ahead, into the register set of the chunk's parity
+  // (its registers allow two sets): chunk kc + 2 in step kc, stored at the end of step kc + 1
+  Regs rg2[2];
   auto step = [&](int kc) {
     const int buf = kc & 1;
-    if (kc + 1 < nch) gload(kc + 1, rg);
+    if constexpr (!kDirect) {
+      if (kc + 1 < nch) gload(kc + 1, rg);
+    }
+    if constexpr (kDirect) {
+      // A = fl(w + e) per tile: e = +-eps by the tile's side, negated where the pair's sign bit
+      // of (row, column) is set; bit position of chunk column c is (c >> 1) | ((c & 1) << 4)
+      const float* wk = reinterpret_cast<const float*>(lds + kWOff) + buf * 32 * kSlRows;
+      const float* xk = reinterpret_cast<const float*>(lds + kXOff) + buf * 32 * kSlCols;
+      const uint32_t* sk = reinterpret_cast<const uint32_t*>(lds + kSOff) + buf * kSlMaxPairs * kSlRows;
+      uint32_t word[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) word[j] = sk[tile_qi[j] * kSlRows + (a_pos ^ ((tile_qi[j] & 15) << 2))];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const float av = wk[a_off + 4 * ks * kSlRows];
+        const uint32_t c = static_cast<uint32_t>(4 * ks + fk);
+        const uint32_t pos = (c >> 1) | ((c & 1u) << 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = __uint_as_float(__float_as_uint(tile_e[j]) ^ (((word[j] >> pos) & 1u) << 31));
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av + e, xk[b_off + 4 * ks * kSlCols + 16 * j], acc[j], 0, 0, 0);
+        }
+      }
+      return;
+    }
     build(buf);
     __syncthreads();
     {
-      const float* wk = reinterpret_cast<const float*>(lds + kSlWOff) + buf * 32 * kSlRows;
-      const float* xk = reinterpret_cast<const float*>(lds + kSlXOff) + buf * 32 * kSlCols;
+      const float* wk = reinterpret_cast<const float*>(lds + kWOff) + buf * 32 * kSlRows;
+      const float* xk = reinterpret_cast<const float*>(lds + kXOff) + buf * 32 * kSlCols;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const float av = wk[a_off + 4 * ks * kSlRows];
@@ -241,7 +294,7 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
       }
     }
     {
-      const char* sk = lds + kSlSOff + buf * kSlMaxPairs * kSlRows * 4 + my_qi * kSlRows * 4;
+      const char* sk = lds + kSOff + buf * kSlMaxPairs * kSlRows * 4 + my_qi * kSlRows * 4;
 #pragma unroll
       for (int i4 = 0; i4 < 2; ++i4) {
         const uint4 w4 = *reinterpret_cast<const uint4*>(sk + 4 * ((8 * rgp + 4 * i4) ^ ((my_qi & 15) << 2)));
@@ -282,10 +335,30 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
     for (int r = 0; r < 4; ++r) bpre[j][r] = bs[r * H];
     cpre[j] = a.first ? 0.f : a.c[static_cast<int64_t>(unit) * a.ncp + col];
   }
-  gload(0, rg);
-  lstore(0, 0, rg);
-  __syncthreads();
-  for (int kc = 0; kc < nch; ++kc) step(kc);
+  if constexpr (kDirect) {
+    // rg2[k & 1] holds chunk k from its request (step k - 2, or the prologue) until it is stored
+    // at the end of step k - 1
+    gload(0, rg2[0]);
+    if (nch > 1) gload(1, rg2[1]);
+    lstore(0, 0, rg2[0]);
+    __syncthreads();
+    for (int kc = 0; kc < nch; kc += 2) {
+      if (kc + 2 < nch) gload(kc + 2, rg2[0]);
+      step(kc);
+      if (kc + 1 < nch) lstore(kc + 1, 1, rg2[1]);
+      __syncthreads();
+      if (kc + 1 >= nch) break;
+      if (kc + 3 < nch) gload(kc + 3, rg2[1]);
+      step(kc + 1);
+      if (kc + 2 < nch) lstore(kc + 2, 0, rg2[0]);
+      __syncthreads();
+    }
+  } else {
+    gload(0, rg);
+    lstore(0, 0, rg);
+    __syncthreads();
+    for (int kc = 0; kc < nch; ++kc) step(kc);
+  }
 
   // last layer: the output weights of the slice's units and the output sign words of the logits
   // role (row v = tid & 63, columns tid >> 6 + 4 i) are requested now, ahead of the cell
@@ -306,12 +379,14 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
 
   // ---- P x to the matrix-core layout, through LDS (the tables are no longer needed) ----
   float* pbuf = reinterpret_cast<float*>(lds);
+  if constexpr (!kDirect) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<float2*>(pbuf + (8 * rgp + i) * kSlPStride + 2 * cp) = accp[i];
-  __syncthreads();
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<float2*>(pbuf + (8 * rgp + i) * kSlPStride + 2 * cp) = accp[i];
+    __syncthreads();
+  }
 
   // ---- cell: lane holds gates 0..3 of unit 4 w + lane / 16 for columns 16 j + lane % 16 ----
-  float* hs = reinterpret_cast<float*>(lds + kSlHsOff);
+  float* hs = reinterpret_cast<float*>(lds + kHsOff);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int cl = 16 * j + fi, col = s0 + cl;
@@ -319,7 +394,8 @@ __global__ __launch_bounds__(kSlThreads, 2) void k_lstm_f32_sliced(F32SlArgs a) 
     const float se = (m & 1) ? -a.eps : a.eps;  // +eps model: W + s eps P; -eps model: W - s eps P
     float g[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) g[r] = fmaf(se, pbuf[(16 * r + ul) * kSlPStride + cl], acc[j][r]) + bpre[j][r];
+    for (int r = 0; r < 4; ++r)
+      g[r] = kDirect ? acc[j][r] + bpre[j][r] : fmaf(se, pbuf[(16 * r + ul) * kSlPStride + cl], acc[j][r]) + bpre[j][r];
     const int64_t at = static_cast<int64_t>(unit) * a.ncp + col;
     float cn, hn;
     lstm_cell(g[0], g[1], g[2], g[3], cpre[j], cn, hn);
