@@ -51,10 +51,13 @@ constexpr int kSlXOff = kSlWOff + 2 * 32 * kSlRows * 4;             // activatio
 constexpr int kSlSOff = kSlXOff + 2 * 32 * kSlCols * 4;             // sign words [2][32 pairs][64 rows]
 constexpr int kSlLdsBytes = kSlSOff + 2 * kSlMaxPairs * kSlRows * 4;  // 80 KB: two workgroups per CU
 constexpr int kSlHsOff = kSlRows * kSlPStride * 4;                  // h [16][64] after the exchange buffer
-// The direct variant (B a multiple of 16) has no tables: h [16][64] at 0, then W^T, activations
-// and sign words as above, 52 KB in all (three workgroups per CU).
+// The direct variant (B a multiple of 16) has no tables and a 64-column block spans at most 3
+// probe pairs: h [16][64] at 0, then W^T, activations and the sign words of 4 pairs, 38 KB in all
+// (four workgroups per CU).
+constexpr int kSlDirWgs = 4;
+constexpr int kSlDirMaxPairs = 4;
 constexpr int kSlDirBase = 4096;
-constexpr int kSlDirLdsBytes = kSlDirBase + (kSlLdsBytes - kSlWOff);
+constexpr int kSlDirLdsBytes = kSlDirBase + (kSlSOff - kSlWOff) + 2 * kSlDirMaxPairs * kSlRows * 4;
 
 typedef float f32x4_sl __attribute__((ext_vector_type(4)));
 // Two floats in LDS by their byte address: the kernel has no static LDS, so its dynamic LDS (and
@@ -92,7 +95,7 @@ struct F32SlArgs {
 // the tile's model (R-8's perturbed weight, rounded once in fp32) and the matrix cores multiply it
 // with the activations. No sign-sum tables, no P x exchange, one barrier per K chunk.
 template <bool kDirect>
-__global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced(F32SlArgs a) {
+__global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f32_sliced(F32SlArgs a) {
   extern __shared__ __align__(16) float sl_lds[];
   char* const lds = reinterpret_cast<char*>(sl_lds);
   // LDS offsets of the staged chunk (the direct variant has no tables in front of them)
@@ -100,6 +103,7 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
   constexpr int kXOff = kWOff + (kSlXOff - kSlWOff);
   constexpr int kSOff = kWOff + (kSlSOff - kSlWOff);
   constexpr int kHsOff = kDirect ? 0 : kSlHsOff;
+  constexpr int kMaxPairs = kDirect ? kSlDirMaxPairs : kSlMaxPairs;  // sign-word pairs per LDS chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, G4 = 4 * H;
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
     const uint32_t* sg = xpart ? a.sg_ih : a.sg_hh;
     const int nw = xpart ? kx : H / 32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kMaxPairs / 4; ++i) {
       const int qi = wave + 4 * i;  // wave-uniform
       rg.s[i] = 0u;
       if (qi < n_q) {
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
   auto lstore = [&](int kc, int buf, const Regs& rg) {
     float* wk = reinterpret_cast<float*>(lds + kWOff) + buf * 32 * kSlRows;
     float* xk = reinterpret_cast<float*>(lds + kXOff) + buf * 32 * kSlCols;
-    uint32_t* sk = reinterpret_cast<uint32_t*>(lds + kSOff) + buf * kSlMaxPairs * kSlRows;
+    uint32_t* sk = reinterpret_cast<uint32_t*>(lds + kSOff) + buf * kMaxPairs * kSlRows;
 #pragma unroll
     for (int i = 0; i < 8; ++i) wk[tid + 256 * i] = rg.w[i];
     if (kc < kx && emb_in) {
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
       for (int i = 0; i < 8; ++i) xk[(wave + 4 * i) * kSlCols + scol] = rg.x[i];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kMaxPairs / 4; ++i) {
       // pair qi's 64 words are stored with their 4-word groups permuted by qi (bits 2-5 of the
       // position xor 4 (qi & 15)), so that the 16-byte reads of lanes with different pairs fall
       // in different banks
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = min(min(s0 + 16 * j, a.ncols - 1) / a.B, 2 * a.pc - 1);
-    tile_qi[j] = min((m >> 1) - q_first, kSlMaxPairs - 1);
+    tile_qi[j] = min((m >> 1) - q_first, kMaxPairs - 1);
     tile_e[j] = (m & 1) ? -a.eps : a.eps;
   }
   // ---- sign-sum role: thread (column pair cp = tid & 31, row group rg = tid >> 5) owns columns
@@ -250,9 +254,6 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
   // Chunk kc + 1 is requested at the top of step kc and written to LDS buffer (kc + 1) & 1 at its
   // end.
   Regs rg;
-  // the direct variant requests two chunks ahead, into the register set of the chunk's parity
-  // (its registers allow two sets): chunk kc + 2 in step kc, stored at the end of step kc + 1
-  Regs rg2[2];
   auto step = [&](int kc) {
     const int buf = kc & 1;
     if constexpr (!kDirect) {
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
       // of (row, column) is set; bit position of chunk column c is (c >> 1) | ((c & 1) << 4)
       const float* wk = reinterpret_cast<const float*>(lds + kWOff) + buf * 32 * kSlRows;
       const float* xk = reinterpret_cast<const float*>(lds + kXOff) + buf * 32 * kSlCols;
-      const uint32_t* sk = reinterpret_cast<const uint32_t*>(lds + kSOff) + buf * kSlMaxPairs * kSlRows;
+      const uint32_t* sk = reinterpret_cast<const uint32_t*>(lds + kSOff) + buf * kMaxPairs * kSlRows;
       uint32_t word[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) word[j] = sk[tile_qi[j] * kSlRows + (a_pos ^ ((tile_qi[j] & 15) << 2))];
@@ -336,21 +337,15 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? 3 : 2) void k_lstm_f32_sliced
     cpre[j] = a.first ? 0.f : a.c[static_cast<int64_t>(unit) * a.ncp + col];
   }
   if constexpr (kDirect) {
-    // rg2[k & 1] holds chunk k from its request (step k - 2, or the prologue) until it is stored
-    // at the end of step k - 1
-    gload(0, rg2[0]);
-    if (nch > 1) gload(1, rg2[1]);
-    lstore(0, 0, rg2[0]);
+    // one chunk ahead: a deeper request queue needs a second register set, and the 158 registers
+    // it takes leave three workgroups per CU, which measured slower than four
+    gload(0, rg);
+    lstore(0, 0, rg);
     __syncthreads();
-    for (int kc = 0; kc < nch; kc += 2) {
-      if (kc + 2 < nch) gload(kc + 2, rg2[0]);
+    for (int kc = 0; kc < nch; ++kc) {
+      if (kc + 1 < nch) gload(kc + 1, rg);
       step(kc);
-      if (kc + 1 < nch) lstore(kc + 1, 1, rg2[1]);
-      __syncthreads();
-      if (kc + 1 >= nch) break;
-      if (kc + 3 < nch) gload(kc + 3, rg2[1]);
-      step(kc + 1);
-      if (kc + 2 < nch) lstore(kc + 2, 0, rg2[0]);
+      if (kc + 1 < nch) lstore(kc + 1, (kc + 1) & 1, rg);
       __syncthreads();
     }
   } else {
