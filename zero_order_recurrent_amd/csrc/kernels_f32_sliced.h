@@ -51,9 +51,10 @@ constexpr int kSlXOff = kSlWOff + 2 * 32 * kSlRows * 4;             // activatio
 constexpr int kSlSOff = kSlXOff + 2 * 32 * kSlCols * 4;             // sign words [2][32 pairs][64 rows]
 constexpr int kSlLdsBytes = kSlSOff + 2 * kSlMaxPairs * kSlRows * 4;  // 80 KB: two workgroups per CU
 constexpr int kSlHsOff = kSlRows * kSlPStride * 4;                  // h [16][64] after the exchange buffer
-// The direct variant (B a multiple of 16) has no tables and a 64-column block spans at most 3
-// probe pairs: h [16][64] at 0, then W^T, activations and the sign words of 4 pairs, 38 KB in all
-// (four workgroups per CU).
+// The direct variant (B a multiple of 16) has no tables, and a 64-column block spans at most two
+// probe pairs (pairs start at multiples of 2B, a multiple of 32; blocks at multiples of 64): h
+// [16][64] at 0, then W^T, activations and the sign words of up to 4 pairs (one per wave), 38 KB
+// in all (four workgroups per CU).
 constexpr int kSlDirWgs = 4;
 constexpr int kSlDirMaxPairs = 4;
 constexpr int kSlDirBase = 4096;
