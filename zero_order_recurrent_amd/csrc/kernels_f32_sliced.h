@@ -51,6 +51,8 @@ constexpr int kSlXOff = kSlWOff + 2 * 32 * kSlRows * 4;             // activatio
 constexpr int kSlSOff = kSlXOff + 2 * 32 * kSlCols * 4;             // sign words [2][32 pairs][64 rows]
 constexpr int kSlLdsBytes = kSlSOff + 2 * kSlMaxPairs * kSlRows * 4;  // 80 KB: two workgroups per CU
 constexpr int kSlHsOff = kSlRows * kSlPStride * 4;                  // h [16][64] after the exchange buffer
+// after the K loop the W^T buffers hold the last layer's output weights [16][V] and sign words
+static_assert((kSlUnits * kSlMaxV + kSlMaxPairs * kSlCols) * 4 <= kSlXOff - kSlWOff, "logit staging");
 // The direct variant (B a multiple of 16) has no tables, and a 64-column block spans at most two
 // probe pairs (pairs start at multiples of 2B, a multiple of 32; blocks at multiples of 64): h
 // [16][64] at 0, then W^T, activations and the sign words of up to 4 pairs (one per wave), 38 KB
@@ -356,20 +358,26 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
     for (int kc = 0; kc < nch; ++kc) step(kc);
   }
 
-  // last layer: the output weights of the slice's units and the output sign words of the logits
-  // role (row v = tid & 63, columns tid >> 6 + 4 i) are requested now, ahead of the cell
-  const int v = tid & 63;
-  float wv[kSlUnits];
-  uint32_t wo[kSlCols / 4];
-  if (a.last && v < a.V) {
+  // last layer: the output weights of the slice's units (rows u0 .. u0 + 15 of W_out^T, 16 V
+  // contiguous floats) and the output sign words of the block's pairs are requested now, ahead of
+  // the cell, and staged in LDS after it
+  constexpr int kOutW = kSlUnits * kSlMaxV / kSlThreads;
+  float wo_r[kOutW];
+  uint32_t so_r[kMaxPairs / 4];
+  if (a.last) {
+    const float* wsrc = a.wt_out + static_cast<int64_t>(u0) * a.V;
+#pragma unroll
+    for (int i = 0; i < kOutW; ++i) {
+      const int idx = tid + kSlThreads * i;
+      wo_r[i] = idx < kSlUnits * a.V ? wsrc[idx] : 0.f;
+    }
     const int wi = u0 >> 5;  // the 16 units lie in one 32-column sign word
 #pragma unroll
-    for (int u = 0; u < kSlUnits; ++u) wv[u] = a.wt_out[static_cast<int64_t>(u0 + u) * a.V + v];
-#pragma unroll
-    for (int i = 0; i < kSlCols / 4; ++i) {
-      const int col = min(s0 + (tid >> 6) + 4 * i, a.ncols - 1);
-      const int q = (col / a.B) >> 1;
-      wo[i] = a.sg_out[(static_cast<int64_t>(q) * (H >> 5) + wi) * a.V + v];
+    for (int i = 0; i < kMaxPairs / 4; ++i) {
+      const int qi = wave + 4 * i;  // wave-uniform
+      so_r[i] = 0u;
+      if (qi < n_q && lane < a.V)
+        so_r[i] = a.sg_out[(static_cast<int64_t>(q_first + qi) * (H >> 5) + wi) * a.V + lane];
     }
   }
 
@@ -403,22 +411,34 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
   }
   if (!a.last) return;
 
-  // ---- partial logits of the slice's 16 units: thread (row v = tid & 63, columns tid >> 6 + 4 i),
-  // so that a wave writes V consecutive floats of zpart [slice][column][V]
-  __syncthreads();
-  if (v >= a.V) return;
+  // ---- partial logits of the slice's 16 units. The W^T buffers are free after the K loop: they
+  // take the output weights [16][V] and the sign words [pair][64]. Item e of the block is
+  // (column e / V, logit e % V), so that consecutive threads write consecutive floats of zpart
+  // [slice][column][V] and every lane has work whatever V is.
+  float* ws = reinterpret_cast<float*>(lds + kWOff);
+  uint32_t* so = reinterpret_cast<uint32_t*>(lds + kWOff) + kSlUnits * kSlMaxV;
 #pragma unroll
-  for (int i = 0; i < kSlCols / 4; ++i) {
-    const int cl = (tid >> 6) + 4 * i, col = s0 + cl;
-    if (col >= a.ncols) break;
+  for (int i = 0; i < kOutW; ++i) {
+    const int idx = tid + kSlThreads * i;
+    if (idx < kSlUnits * a.V) ws[idx] = wo_r[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxPairs / 4; ++i) so[(wave + 4 * i) * kSlCols + lane] = so_r[i];
+  __syncthreads();
+  const int n_items = min(kSlCols, a.ncols - s0) * a.V;
+  for (int e = tid; e < n_items; e += kSlThreads) {
+    const int cl = static_cast<int>(static_cast<uint32_t>(e) / static_cast<uint32_t>(a.V));
+    const int v = e - cl * a.V;
+    const int col = s0 + cl;
     const int m = col / a.B;
-    const uint32_t word = wo[i];
+    const uint32_t word = so[((m >> 1) - q_first) * kSlCols + v];
     float z = 0.f;
 #pragma unroll
     for (int u = 0; u < kSlUnits; ++u) {
       const uint32_t cidx = static_cast<uint32_t>(u0 + u);
-      const float e = signed_eps(a.eps, (word >> sign_bit_pos(cidx & 31u)) & 1u);
-      const float wp = (m & 1) ? wv[u] - e : wv[u] + e;
+      const float pe = signed_eps(a.eps, (word >> sign_bit_pos(cidx & 31u)) & 1u);
+      const float w = ws[u * a.V + v];
+      const float wp = (m & 1) ? w - pe : w + pe;
       z = fmaf(wp, hs[u * kSlCols + cl], z);
     }
     a.zpart[(static_cast<int64_t>(blockIdx.x) * a.ncp + col) * a.V + v] = z;
