@@ -55,6 +55,9 @@ SMALL = {
     "f32sl_direct_chunks": b.make_config(2, 11, 32, 64, 16, 4, 15, "f32", 1e-3, 1e-3, 93, probes_per_chunk=10),
     # the direct variant with 32 sequences per model (two models per 64-column block), V = 64
     "f32sl_direct_b32": b.make_config(1, 64, 64, 96, 32, 3, 5, "f32", 1e-3, 1e-3, 94),
+    # B a multiple of 64 (every column block in one model: one perturbed A value per K step for
+    # the block's four tiles), two layers, 128 sequences per model (two blocks each)
+    "f32sl_direct_b128": b.make_config(2, 20, 32, 64, 128, 3, 3, "f32", 1e-3, 1e-3, 95),
 }
 
 

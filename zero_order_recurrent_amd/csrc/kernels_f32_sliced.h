@@ -242,6 +242,9 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
     tile_qi[j] = min((m >> 1) - q_first, kMaxPairs - 1);
     tile_e[j] = (m & 1) ? -a.eps : a.eps;
   }
+  // B a multiple of 64: the block's 64 columns are sequences of one model (blocks start at
+  // multiples of 64)
+  const bool one_model = a.B % 64 == 0;
   // ---- sign-sum role: thread (column pair cp = tid & 31, row group rg = tid >> 5) owns columns
   // 2 cp, 2 cp + 1 and positions p = 8 rg + i. Columns 2k and 2k + 1 always belong to one probe
   // pair (a pair's 2B columns start at a multiple of 2B), so they share the nibble and one 8-byte
@@ -268,6 +271,22 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
       const float* wk = reinterpret_cast<const float*>(lds + kWOff) + buf * 32 * kSlRows;
       const float* xk = reinterpret_cast<const float*>(lds + kXOff) + buf * 32 * kSlCols;
       const uint32_t* sk = reinterpret_cast<const uint32_t*>(lds + kSOff) + buf * kMaxPairs * kSlRows;
+      if (one_model) {
+        // all four tiles in one model: one A value per K step feeds the four MFMAs
+        const uint32_t word = sk[tile_qi[0] * kSlRows + (a_pos ^ ((tile_qi[0] & 15) << 2))];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const float av = wk[a_off + 4 * ks * kSlRows];
+          const uint32_t c = static_cast<uint32_t>(4 * ks + fk);
+          const uint32_t pos = (c >> 1) | ((c & 1u) << 4);
+          const float e = __uint_as_float(__float_as_uint(tile_e[0]) ^ (((word >> pos) & 1u) << 31));
+          const float ap = av + e;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, xk[b_off + 4 * ks * kSlCols + 16 * j], acc[j], 0, 0, 0);
+        }
+        return;
+      }
       uint32_t word[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) word[j] = sk[tile_qi[j] * kSlRows + (a_pos ^ ((tile_qi[j] & 15) << 2))];
