@@ -377,19 +377,16 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
     for (int kc = 0; kc < nch; ++kc) step(kc);
   }
 
-  // last layer: the output weights of the slice's units (rows u0 .. u0 + 15 of W_out^T, 16 V
-  // contiguous floats) and the output sign words of the block's pairs are requested now, ahead of
-  // the cell, and staged in LDS after it
-  constexpr int kOutW = kSlUnits * kSlMaxV / kSlThreads;
+  // last layer: the output weights of the slice's units (W_out^T rows u0 .. u0 + 15; wave w
+  // reads rows w + 4 i, lane = logit) and the output sign words of the block's pairs are
+  // requested now, ahead of the cell, and staged in LDS after it
+  constexpr int kOutW = kSlUnits / 4;
   float wo_r[kOutW];
   uint32_t so_r[kMaxPairs / 4];
   if (a.last) {
-    const float* wsrc = a.wt_out + static_cast<int64_t>(u0) * a.V;
 #pragma unroll
-    for (int i = 0; i < kOutW; ++i) {
-      const int idx = tid + kSlThreads * i;
-      wo_r[i] = idx < kSlUnits * a.V ? wsrc[idx] : 0.f;
-    }
+    for (int i = 0; i < kOutW; ++i)
+      wo_r[i] = lane < a.V ? a.wt_out[static_cast<int64_t>(u0 + wave + 4 * i) * a.V + lane] : 0.f;
     const int wi = u0 >> 5;  // the 16 units lie in one 32-column sign word
 #pragma unroll
     for (int i = 0; i < kMaxPairs / 4; ++i) {
@@ -431,33 +428,31 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
   if (!a.last) return;
 
   // ---- partial logits of the slice's 16 units. The W^T buffers are free after the K loop: they
-  // take the output weights [16][V] and the sign words [pair][64]. Item e of the block is
+  // take the output weights [16 units][64] and the sign words [pair][64]. Item e of the block is
   // (column e / V, logit e % V), so that consecutive threads write consecutive floats of zpart
   // [slice][column][V] and every lane has work whatever V is.
   float* ws = reinterpret_cast<float*>(lds + kWOff);
   uint32_t* so = reinterpret_cast<uint32_t*>(lds + kWOff) + kSlUnits * kSlMaxV;
 #pragma unroll
-  for (int i = 0; i < kOutW; ++i) {
-    const int idx = tid + kSlThreads * i;
-    if (idx < kSlUnits * a.V) ws[idx] = wo_r[i];
-  }
+  for (int i = 0; i < kOutW; ++i) ws[(wave + 4 * i) * kSlCols + lane] = wo_r[i];
 #pragma unroll
   for (int i = 0; i < kMaxPairs / 4; ++i) so[(wave + 4 * i) * kSlCols + lane] = so_r[i];
   __syncthreads();
+  // units u0 .. u0 + 15 are columns 0-15 or 16-31 of their sign word; shifted right by `half`, the
+  // bit of unit u0 + u is at (u & 1) 16 + (u >> 1) either way
+  const uint32_t half = static_cast<uint32_t>(u0 & 16) >> 1;
   const int n_items = min(kSlCols, a.ncols - s0) * a.V;
   for (int e = tid; e < n_items; e += kSlThreads) {
     const int cl = static_cast<int>(static_cast<uint32_t>(e) / static_cast<uint32_t>(a.V));
     const int v = e - cl * a.V;
     const int col = s0 + cl;
     const int m = col / a.B;
-    const uint32_t word = so[((m >> 1) - q_first) * kSlCols + v];
+    // the -eps model of a pair takes the opposite sign: w - s eps = w + (-s) eps exactly
+    const uint32_t word = (so[((m >> 1) - q_first) * kSlCols + v] >> half) ^ ((m & 1) ? 0xFFFFFFFFu : 0u);
     float z = 0.f;
 #pragma unroll
     for (int u = 0; u < kSlUnits; ++u) {
-      const uint32_t cidx = static_cast<uint32_t>(u0 + u);
-      const float pe = signed_eps(a.eps, (word >> sign_bit_pos(cidx & 31u)) & 1u);
-      const float w = ws[u * a.V + v];
-      const float wp = (m & 1) ? w - pe : w + pe;
+      const float wp = ws[u * kSlCols + v] + signed_eps(a.eps, (word >> ((u & 1) * 16 + (u >> 1))) & 1u);
       z = fmaf(wp, hs[u * kSlCols + cl], z);
     }
     a.zpart[(static_cast<int64_t>(blockIdx.x) * a.ncp + col) * a.V + v] = z;
