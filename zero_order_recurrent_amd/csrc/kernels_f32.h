@@ -356,14 +356,28 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
       for (int i = 0; i < M; ++i) acc[i] = 0.f;
       uint32_t word[G];
       const float* wo = a.wt_out + static_cast<int64_t>(k0) * V + v;  // W_out^T column k, row v
-      for (int k = k0; k < k1; ++k) {
-        if (k == k0 || (k & 31) == 0) {
+      // columns in groups of 8: the group's weights and the (at most two) sign words its columns
+      // fall in are requested together
+      for (int kb = k0; kb < k1; kb += 8) {
+        float wk[8];
+        uint32_t wa[G], wb[G];
+        const int kl = min(kb + 7, k1 - 1);
 #pragma unroll
-          for (int g = 0; g < G; ++g) word[g] = (a.sg_out + (static_cast<int64_t>(qg[g]) * nw + (k >> 5)) * V)[v];
+        for (int i = 0; i < 8; ++i) wk[i] = kb + i < k1 ? wo[static_cast<int64_t>(kb - k0 + i) * V] : 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t* sg = a.sg_out + static_cast<int64_t>(qg[g]) * nw * V + v;
+          wa[g] = sg[static_cast<int64_t>(kb >> 5) * V];
+          wb[g] = sg[static_cast<int64_t>(kl >> 5) * V];
         }
-        const float w = *wo;
-        wo += V;
-        f32_column<G, NB>(acc, w, hl + k * M, word, sign_bit_pos(static_cast<uint32_t>(k)), a.eps);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int k = kb + i;
+          if (k >= k1) break;
+#pragma unroll
+          for (int g = 0; g < G; ++g) word[g] = (k >> 5) == (kb >> 5) ? wa[g] : wb[g];
+          f32_column<G, NB>(acc, wk[i], hl + k * M, word, sign_bit_pos(static_cast<uint32_t>(k)), a.eps);
+        }
       }
       f32_store_slots<M>(gbuf + (j * V + v) * M, acc);
     }
@@ -375,14 +389,20 @@ __global__ __launch_bounds__(kF32MaxThreads) void k_lstm_f32(F32Args a) {
       z[i] = s;
     }
     __syncthreads();
-    // Cross-entropy per slot. The next writes of z and gbuf come after the next barriers.
-    if (tid < M) {
-      const int slot = tid, b = slot % NB;
-      if (b < nb) {
-        float zmax = z[slot];
-        for (int v = 1; v < V; ++v) zmax = fmaxf(zmax, z[v * M + slot]);
-        float sum = 0.f;
-        for (int v = 0; v < V; ++v) sum += expf(z[v * M + slot] - zmax);
+    // Cross-entropy per slot, one wave per slot (lane l: logits l, l + 64, ...; NT is whole
+    // waves). The next writes of z and gbuf come after the next barriers.
+    for (int slot = tid >> 6; slot < M; slot += NT >> 6) {
+      const int lane = tid & 63, b = slot % NB;
+      if (b >= nb) continue;  // whole waves
+      float zmax = -INFINITY;
+      for (int v = lane; v < V; v += 64) zmax = fmaxf(zmax, z[v * M + slot]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o));
+      float sum = 0.f;
+      for (int v = lane; v < V; v += 64) sum += expf(z[v * M + slot] - zmax);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      if (lane == 0) {
         const int y = a.tg[static_cast<int64_t>(b0 + b) * a.tg_stride + t];
         if (y >= 0) loss[slot] += (zmax + logf(sum)) - z[min(y, V - 1) * M + slot];
       }
