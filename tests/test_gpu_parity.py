@@ -267,20 +267,30 @@ def test_invalid_tokens_give_nan_losses():
     run.close()
 
 
-@pytest.mark.parametrize("name", ["bf16_ragged", "f32_ragged"])
-def test_deterministic_and_chunk_invariant(name):
+# (case, chunk sizes): every chunk size keeps the case on one forward kernel, whose per-column
+# arithmetic does not depend on which other models share a launch; the row-sliced cases need
+# 2 P B >= 256 columns per chunk (the table variant, the direct one, and the direct one with one
+# model per column block)
+@pytest.mark.parametrize("name,ppcs", [("bf16_ragged", (0, 1, 2, 0)), ("f32_ragged", (0, 1, 2, 0)),
+                                       ("f32sl_b9_chunks", (0, 15, 20, 0)),
+                                       ("f32sl_direct_chunks", (0, 8, 10, 0)),
+                                       ("f32sl_direct_b128", (0, 1, 2, 0))])
+def test_deterministic_and_chunk_invariant(name, ppcs):
     c = SMALL[name]
     say(f"[gpu] determinism {name}")
     theta, tokens = _inputs(c, 8)
     outs = []
-    for ppc in (0, 1, 2, 0):
+    kernels = set()
+    for ppc in ppcs:
         cc = b.make_config(c.n_layers, c.vocab, c.embed, c.hidden, c.batch, c.seq_len, c.n_probes,
                            dtype_name(c), c.eps, c.lr, c.base_seed, probes_per_chunk=ppc)
         run = HipRun(cc, theta, tokens)
+        kernels.add(b.cdrge_timed_kernel(run.ctx.ctx, 0))
         losses, seq, st = run.probe_losses(1)
         assert st == 0
         outs.append((losses, seq))
         run.close()
+    assert len(kernels) == 1, kernels
     for l, s in outs[1:]:
         np.testing.assert_array_equal(l, outs[0][0])
         np.testing.assert_array_equal(s, outs[0][1])
