@@ -211,6 +211,33 @@ def test_update_parity_many_tensors(oracle):
     run.close()
 
 
+# eta = 0 (allowed: the configuration only requires eta >= 0): the coefficient eta / (2 K eps) is
+# zero, so every update kernel must leave theta bit-identical whatever the loss differences (theta
+# holds no exact zeros, whose sign the subtraction of a zero may change).
+@pytest.mark.parametrize("dtype,layers,n_probes,kernel", [("bf16", 2, 8, "k_update_perm"),
+                                                          ("f32", 2, 8, "k_update_lut"),
+                                                          ("bf16", 2, 96, "k_update_lut"),
+                                                          ("bf16", 10, 12, "k_update")])
+def test_zero_learning_rate_leaves_theta(oracle, dtype, layers, n_probes, kernel):
+    if layers == 10:
+        c = b.make_config(10, 20, 32, 32, 2, 2, n_probes, dtype, 1e-3, 0.0, 97)
+    else:
+        c = b.make_config(layers, 50, 64, 192, 3, 2, n_probes, dtype, 1e-3, 0.0, 96)
+    say(f"[gpu] zero learning rate, {kernel}, {dtype}, K={n_probes}")
+    theta, tokens = _inputs(c, 13)
+    assert (as_f64(theta) != 0).all()
+    rng = np.random.default_rng(7)
+    losses = (3.0 + 1e-2 * rng.standard_normal(2 * c.n_probes)).astype(np.float32)
+    run = HipRun(c, theta, tokens)
+    assert b.cdrge_timed_kernel(run.ctx.ctx, 2) == kernel
+    assert run.update(5, losses) == 0
+    np.testing.assert_array_equal(run.theta(), theta)
+    ref = theta.copy()
+    assert oracle.update(ocfg(c), ref, 5, losses) == 0
+    np.testing.assert_array_equal(ref, theta)
+    run.close()
+
+
 def test_update_many_segments(oracle):
     # bf16, K = 16, d = 16.1M: each update workgroup strides over the 128-column segments several
     # times (both parameter buffers in turn, and a partial last pass); W_ih has 1,056 columns, so
