@@ -58,6 +58,12 @@ SMALL = {
     # B a multiple of 64 (every column block in one model: one perturbed A value per K step for
     # the block's four tiles), two layers, 128 sequences per model (two blocks each)
     "f32sl_direct_b128": b.make_config(2, 20, 32, 64, 128, 3, 3, "f32", 1e-3, 1e-3, 95),
+    # the largest sizes the library accepts: K = 1,024 probe pairs (every pair its own perturbed
+    # models) with the most fp32 layers (8) on the persistent kernel, 8 layers on the row-sliced
+    # kernels, and K = 1,024 in bf16 (one sequence per model, 1,024 column blocks)
+    "f32_max_k_layers": b.make_config(8, 7, 12, 8, 2, 2, 1024, "f32", 1e-3, 1e-3, 100),
+    "f32sl_l8": b.make_config(8, 10, 32, 32, 8, 2, 16, "f32", 1e-3, 1e-3, 101),
+    "bf16_max_k": b.make_config(1, 5, 32, 32, 1, 2, 1024, "bf16", 1e-2, 1e-2, 102),
 }
 
 
@@ -149,7 +155,7 @@ def test_signs_bit_exact_through_update(oracle, dtype):
 # copies (one or two 64 KB regions). Otherwise K = 24, 300 and 600 keep 4, 2 and 1 copies of the
 # probe-group tables in LDS.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n_probes", [8, 13, 24, 40, 57, 64, 300, 600])
+@pytest.mark.parametrize("n_probes", [8, 13, 24, 40, 57, 64, 300, 600, 1024])
 def test_update_parity_identical_losses(oracle, dtype, n_probes):
     c = b.make_config(2, 50, 64, 192, 3, 2, n_probes, dtype, 1e-3, 1e-3, 99)
     say(f"[gpu] update parity {dtype} K={n_probes}")
