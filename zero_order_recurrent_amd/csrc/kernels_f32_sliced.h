@@ -51,7 +51,8 @@ constexpr int kSlXOff = kSlWOff + 2 * 32 * kSlRows * 4;             // activatio
 constexpr int kSlSOff = kSlXOff + 2 * 32 * kSlCols * 4;             // sign words [2][32 pairs][64 rows]
 constexpr int kSlLdsBytes = kSlSOff + 2 * kSlMaxPairs * kSlRows * 4;  // 80 KB: two workgroups per CU
 constexpr int kSlHsOff = kSlRows * kSlPStride * 4;                  // h [16][64] after the exchange buffer
-// after the K loop the W^T buffers hold the last layer's output weights [16][V] and sign words
+// after the K loop the W^T buffers hold the last layer's output weights [16 units][64] and output
+// sign words [pairs][64]
 static_assert((kSlUnits * kSlMaxV + kSlMaxPairs * kSlCols) * 4 <= kSlXOff - kSlWOff, "logit staging");
 // The direct variant (B a multiple of 16) has no tables, and a 64-column block spans at most two
 // probe pairs (pairs start at multiples of 2B, a multiple of 32; blocks at multiples of 64): h
@@ -95,8 +96,8 @@ struct F32SlArgs {
 //
 // kDirect: when B is a multiple of 16, every 16-column matrix-core tile lies in one model, so the
 // perturbed weight itself can be the A operand: each lane forms fl(w +- eps p) for its element of
-// the tile's model (R-8's perturbed weight, rounded once in fp32) and the matrix cores multiply it
-// with the activations. No sign-sum tables, no P x exchange, one barrier per K chunk.
+// the tile's model (the perturbed weight w + s eps p rounded once to fp32, as a perturbed copy of
+// the parameters holds it) and the matrix cores multiply it with the activations. No sign-sum tables, no P x exchange, one barrier per K chunk.
 template <bool kDirect>
 __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f32_sliced(F32SlArgs a) {
   extern __shared__ __align__(16) float sl_lds[];
