@@ -295,6 +295,9 @@ def main():
     ap.add_argument("--workload", default="lstm1b")
     ap.add_argument("--seq-len", type=int, default=0,
                     help="override the workload's sequence length T (same model, batch and probes)")
+    ap.add_argument("--probes-per-chunk", type=int, default=-1,
+                    help="override the workload's probe pairs per chain of forward launches (0: all K "
+                         "pairs at once); K / G is one GPU's share of a run over G GPUs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -329,6 +332,8 @@ def main():
             print("--seq-len applies to the language-model workloads", file=sys.stderr)
             sys.exit(2)
         p = p.with_(seq_len=args.seq_len)
+    if args.probes_per_chunk >= 0:
+        p = p.with_(probes_per_chunk=args.probes_per_chunk)
     theta_host = make_theta(p, _param_count(p))
     lm = p.task == "lm"
     tokens_host = make_tokens(p) if lm else None
