@@ -57,16 +57,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_tag: str, workload: str):
+def traffic_from_profiles(kernel_tag: str, workload: str, probes_per_chunk: int):
     """HBM bytes per launch of a kernel from the committed counter summary (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy of known size), if it was taken on the current kernel
-    sources; otherwise None."""
+    sources with the same probe pairs per launch; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("probes_per_chunk") != probes_per_chunk:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -411,8 +411,8 @@ def main():
     gate_bound = "mfma" if bf16 or gate_kernel == "k_lstm_f32_sliced" else "alu"
     traffic = traffic_from_profiles({"k_lstm_gates_bf16": "gates_bf16", "k_lstm_f32": "lstm_f32",
                                      "k_lstm_f32_sliced": "lstm_f32_sliced"}.get(gate_kernel, gate_kernel),
-                                    args.workload)
-    upd_traffic = traffic_from_profiles("update_bf16" if bf16 else "update_f32", args.workload)
+                                    args.workload, p.probes_per_chunk)
+    upd_traffic = traffic_from_profiles("update_bf16" if bf16 else "update_f32", args.workload, p.probes_per_chunk)
     upd_ms, upd_n = timing[2]
     upd_gbs = work[2] / (upd_ms / 1e3) / 1e9 if upd_n else 0.0
     ce_ms, ce_n = timing[1]

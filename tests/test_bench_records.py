@@ -66,14 +66,16 @@ def test_record_contract(path):
 def test_traffic_lookup_follows_source_hash(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    rec = {"kernel_source_hash": "abc123", "hbm_bytes_per_launch": 12345.0}
+    rec = {"kernel_source_hash": "abc123", "probes_per_chunk": 4, "hbm_bytes_per_launch": 12345.0}
     (prof / "gates_bf16_demo_traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc123")
-    assert bench.traffic_from_profiles("gates_bf16", "demo") == 12345.0
+    assert bench.traffic_from_profiles("gates_bf16", "demo", 4) == 12345.0
+    # another launch shape (pairs per launch) is not the launch the counters measured
+    assert bench.traffic_from_profiles("gates_bf16", "demo", 8) is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
-    assert bench.traffic_from_profiles("gates_bf16", "demo") is None
-    assert bench.traffic_from_profiles("gates_bf16", "missing") is None
+    assert bench.traffic_from_profiles("gates_bf16", "demo", 4) is None
+    assert bench.traffic_from_profiles("gates_bf16", "missing", 4) is None
 
 
 def test_source_hash_ignores_comments(tmp_path, monkeypatch):

@@ -60,7 +60,9 @@ PRESETS = {
     "tiny": Preset("tiny", 1, 1, 16, 32, 16, "f32", 4, 10, 8, 1e-3, 1e-3, "uniform", steps=3),
     "overfit": Preset("overfit", 2, 1, 64, 256, 32, "f32", 1, 100, 512, 1e-3, 1e-3, "uniform"),
     "charlm": Preset("charlm", 3, 2, 128, 1024, 50, "bf16", 1024, 10, 64, 1e-4, 1e-4, "zipf"),
-    "lstm270m": Preset("lstm270m", 4, 2, 4096, 4096, 50, "bf16", 1024, 10, 32, 1e-4, 1e-4, "zipf"),
+    # chunks of 4 pairs: a launch's activations (134 MB) stay in the Infinity Cache
+    "lstm270m": Preset("lstm270m", 4, 2, 4096, 4096, 50, "bf16", 1024, 10, 32, 1e-4, 1e-4, "zipf",
+                       probes_per_chunk=4),
     "lstm1b": Preset("lstm1b", 5, 4, 5888, 5888, 50, "bf16", 256, 10, 16, 1e-4, 1e-4, "zipf",
                      probes_per_chunk=8),
     # the char-LM workload (same data: index 3) in the exact-perturbation bf16 dtype
