@@ -381,13 +381,18 @@ cdrge_status enqueue_f32_sliced(cdrge_ctx* ctx, const TokenRefs& tr, int pair0, 
       g.wt_out = ctx->at<float>(p.off_wt[tout.id]);
       g.sg_out = ctx->at<uint32_t>(p.off_sg[tout.id]);
       g.zpart = zp;
+      g.tg = tr.tg;
+      g.tg_stride = tr.tg_stride;
       g.eps = eps;
       g.in = static_cast<int>(tih.cols);
       g.H = p.H; g.B = p.B; g.V = p.V; g.L = p.L; g.layer = l; g.t = t;
       g.ncols = ncols; g.ncp = ncp; g.pc = pc; g.in_stride = tr.in_stride;
       g.first = t == 0; g.last = l == p.L - 1;
+      // the last layer's logits count only when every target is scored: otherwise a column's
+      // logits are formed where its target is scored, which the host does not see, and the count
+      // keeps the gate products alone
       const double flops = 2.0 * 4 * p.H * (double(tih.cols) + (t > 0 ? p.H : 0)) * ncols +
-                           (l == p.L - 1 ? 2.0 * p.V * p.H * ncols : 0.0);
+                           (l == p.L - 1 && !tr.allow_unscored ? 2.0 * p.V * p.H * ncols : 0.0);
       CDRGE_TRY(timed(ctx, 0, flops, [&] {
         if (p.B % 16 == 0)
           hipLaunchKernelGGL(k_lstm_f32_sliced<true>, grid, dim3(kSlThreads), kSlDirLdsBytes, s, g);

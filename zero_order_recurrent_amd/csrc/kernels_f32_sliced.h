@@ -23,7 +23,8 @@
 // lane of the matrix-core output (local row 4u + g is gate g of unit u), so the LSTM cell runs in
 // registers; c and h live in global memory as [H][columns], h ping-ponged per layer.
 //
-// The last layer also forms, for its 16 units, the partial logits of every column:
+// The last layer also forms, for its 16 units, the partial logits of every column whose target at
+// t is scored (the others add nothing to their loss):
 // zpart[slice][column][v] = sum over its units u of fl(w_out[v][u] +- eps_vu) h[u][column], the
 // perturbed output weight rounded once in fp32 as in the persistent kernel; k_ce_f32_sliced adds
 // the slices in order, the perturbed output bias and the cross-entropy of the timestep.
@@ -85,8 +86,9 @@ struct F32SlArgs {
   const float* wt_out;     // last layer: W_out^T [H][V]
   const uint32_t* sg_out;  // [pairs][H / 32][V]
   float* zpart;            // last layer: partial logits [H / 16][ncp][V]
+  const int32_t* tg;       // last layer: target of (sequence b, t) at tg[b * tg_stride + t]
   float eps;
-  int in, H, B, V, L, layer, t, ncols, ncp, pc, in_stride, first, last;
+  int in, H, B, V, L, layer, t, ncols, ncp, pc, in_stride, tg_stride, first, last;
 };
 
 // grid (H / 16, ncp / 64), block 256, dynamic LDS kSlLdsBytes (kDirect: kSlDirLdsBytes). Requires
@@ -448,6 +450,8 @@ __global__ __launch_bounds__(kSlThreads, kDirect ? kSlDirWgs : 2) void k_lstm_f3
     const int v = e - cl * a.V;
     const int col = s0 + cl;
     const int m = col / a.B;
+    // a column whose target at t is not scored adds nothing to its loss: its logits are not formed
+    if (a.tg[static_cast<int64_t>(col - m * a.B) * a.tg_stride + a.t] < 0) continue;
     // the -eps model of a pair takes the opposite sign: w - s eps = w + (-s) eps exactly
     const uint32_t word = (so[((m >> 1) - q_first) * kSlCols + v] >> half) ^ ((m & 1) ? 0xFFFFFFFFu : 0u);
     float z = 0.f;
@@ -471,6 +475,11 @@ __global__ __launch_bounds__(256) void k_ce_f32_sliced(const float* __restrict__
   const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (col >= ncols) return;  // whole waves
   const int m = col / B, b = col - m * B;
+  const int y = tg[static_cast<int64_t>(b) * tg_stride + t];
+  if (y < 0) {  // not scored: the column's partial logits were not formed
+    if (lane == 0 && t == 0) seq[col] = 0.f;
+    return;
+  }
   const bool on = lane < V;
   float z = -INFINITY;
   if (on) {
@@ -495,12 +504,8 @@ __global__ __launch_bounds__(256) void k_ce_f32_sliced(const float* __restrict__
   float e = on ? expf(z - zmax) : 0.f;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) e += __shfl_xor(e, o);
-  const int y = tg[static_cast<int64_t>(b) * tg_stride + t];
-  const float zy = __shfl(z, min(max(y, 0), V - 1));
-  if (lane == 0) {
-    const float loss = y >= 0 ? (zmax + logf(e)) - zy : 0.f;
-    seq[col] = (t == 0 ? 0.f : seq[col]) + loss;
-  }
+  const float zy = __shfl(z, min(y, V - 1));
+  if (lane == 0) seq[col] = (t == 0 ? 0.f : seq[col]) + ((zmax + logf(e)) - zy);
 }
 
 // Per-model perturbed copies of a small fp32 tensor [rows][cols]: out[(m rows + r) out_cols + c]
