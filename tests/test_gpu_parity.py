@@ -287,11 +287,15 @@ def test_nonfinite_loss_leaves_theta(oracle):
     run.close()
 
 
-def test_invalid_tokens_give_nan_losses():
-    c = SMALL["f32_ragged"]
-    say("[gpu] invalid tokens")
+# a token at or above V, or below zero (in the language-model form every target is scored), on
+# each forward kernel: the step's losses are NaN and the update leaves theta alone
+@pytest.mark.parametrize("name", ["f32_ragged", "bf16_ragged", "f32sl_direct_chunks", "f32sl_b9_chunks"])
+@pytest.mark.parametrize("bad", ["vocab", "negative"])
+def test_invalid_tokens_give_nan_losses(name, bad):
+    c = SMALL[name]
+    say(f"[gpu] invalid tokens {name} {bad}")
     theta, tokens = _inputs(c, 7)
-    tokens[3, 2] = c.vocab
+    tokens[3, 2] = c.vocab if bad == "vocab" else -1
     run = HipRun(c, theta, tokens)
     losses, _, st = run.probe_losses(0)
     assert np.isnan(losses).all()
