@@ -116,16 +116,20 @@ def test_language_model_is_the_shifted_io_form(dtype):
     run.close()
 
 
-def test_io_invalid_and_unscored():
-    c = b.make_config(1, 10, 32, 64, 6, 8, 2, "f32", 1e-3, 1e-3, 612)
-    say("[gpu] io form: invalid inputs, invalid targets, nothing scored")
+# B = 6 runs on the persistent fp32 kernel; B = 16 with 8 pairs (256 columns) on the row-sliced
+# one, whose logits and cross-entropy skip unscored targets
+@pytest.mark.parametrize("batch,pairs,kernel", [(6, 2, "k_lstm_f32"), (16, 8, "k_lstm_f32_sliced")])
+def test_io_invalid_and_unscored(batch, pairs, kernel):
+    c = b.make_config(1, 10, 32, 64, batch, 8, pairs, "f32", 1e-3, 1e-3, 612)
+    say(f"[gpu] io form: invalid inputs, invalid targets, nothing scored ({kernel})")
     rng = np.random.default_rng(33)
     theta = rng.uniform(-0.1, 0.1, b.cdrge_param_count(c)).astype(np.float32)
-    inputs, targets = make_transduction("copy", 8, 6, 1, 4, 79)
+    inputs, targets = make_transduction("copy", 8, batch, 1, 4, 79)
     for what, inp, tg in [("input out of range", np.where(np.arange(8) == 3, 10, inputs), targets),
                           ("target out of range", inputs, np.where(targets >= 0, 10, targets)),
                           ("nothing scored", inputs, np.full_like(targets, -1))]:
         run = IoRun(c, theta, inp.astype(np.int32), tg.astype(np.int32))
+        assert b.cdrge_timed_kernel(run.ctx.ctx, 0) == kernel
         losses, _, st = run.probe_losses_io(0)
         assert st == 0
         assert np.isnan(losses).all(), what
