@@ -60,6 +60,9 @@ constexpr int kKChunk = 32;
 constexpr int kAStageBytes = 2 * kTileRows * 64;   // both models' 128 x 32 bf16 tiles
 constexpr int kAStages = 8;
 constexpr int kBRing = 4;                          // activation register ring (chunks)
+// K-step phases (see the step of k_lstm_gates_bf16): every request, or the last two groups of four
+constexpr int kAll = 0, kPenult = 1, kLast = 2;
+constexpr int kPhasedMaxChunks = 64;  // longest reduction (in chunks) run on the phased instance
 // Workgroups resident on one XCD at a time (one per CU, 32 per XCD) cover group_rows row tiles x
 // group_cols column blocks (16 x 2 or 8 x 4, chosen by the host), so that each activation chunk
 // is fetched into that XCD's L2 once for group_rows workgroups and each weight chunk once for
@@ -153,7 +156,12 @@ __global__ void k_tile_gate_weights(const uint16_t* __restrict__ w, int H, int c
 // so that G = W [x; h] +- eps' P [x; h] with no rounding of the perturbed weight. Twice the
 // matrix-core work; A fragments are read one row group ahead (two rings of two) to stay within
 // the register budget of two waves per SIMD.
-template <bool kExact>
+//
+// kPhased: the chunk count (in + H, or in alone at the first timestep, over 32) is a multiple of
+// 4 and at least 8, and the last two groups of four K steps leave out the requests past the end
+// (the host picks the instance, for short reductions; one code path per instance keeps the
+// register budget).
+template <bool kExact, bool kPhased>
 __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
   char* As = reinterpret_cast<char*>(smem);  // [8 stages][model][128 rows][64 B], swizzled
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // into its stage; row groups 6-7 finish, followed by the reads of row groups 0-1 of chunk c+1.
   // Selecting late in the step gives the weight requests more time to arrive. Past the last
   // chunk the requests repeat the last chunk and the select fills a stage that is never
-  // multiplied.
+  // multiplied (the phased instance leaves both out).
   //
   // The selected tiles live in an 8-stage ring (chunk k in stage k % 8), selected 4 chunks ahead,
   // and a barrier follows the select only in every fourth step (S = 3). That is enough:
@@ -305,15 +313,28 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   // Fewer barriers let the waves drift against each other and absorb memory latency.
   uint4 w_r[4];  // weight ring: chunk k in slot k % 4
   uint32_t wd_r[4];
-  auto step = [&](int c, auto S) {
+  // Ph: kAll issues every request and select (clamped to the last chunk past the end); when the
+  // chunk count is a multiple of 4 (and at least 8), the last two groups of four steps run as
+  // kPenult and kLast, which leave out at compile time what would only repeat the last chunk:
+  // kPenult the weight requests of its fourth step (chunks nch, nch + 1); kLast every weight
+  // request and select, the activation requests of its last three steps (chunks nch and up) and
+  // the fragment reads of chunk nch, and its barrier (it writes no LDS, and the selects of chunks
+  // nch - 4 .. nch - 1 are followed by the barrier of kPenult's fourth step). The code stays
+  // straight-line, so the compiler's waits count exactly the requests in flight.
+  auto step = [&](int c, auto S, auto Ph) {
     constexpr int s_ = decltype(S)::value;
+    constexpr int ph = decltype(Ph)::value;
     constexpr int wuse = s_;
+    constexpr bool w_req = s_ % 2 == 1 && ph != kLast && !(ph == kPenult && s_ == 3);
+    constexpr bool b_req = ph != kLast || s_ == 0;
+    constexpr bool sel = ph != kLast;
+    constexpr bool next_reads = !(ph == kLast && s_ == 3);
     const int rs = c & (kAStages - 1), rs1 = (c + 1) & (kAStages - 1), ws = (c + 4) & (kAStages - 1);
-    if constexpr (s_ % 2 == 1) {
+    if constexpr (w_req) {
       load_w(min(c + 5, nch - 1), w_r[(s_ + 1) % 4], wd_r[(s_ + 1) % 4]);
       load_w(min(c + 6, nch - 1), w_r[(s_ + 2) % 4], wd_r[(s_ + 2) % 4]);
     }
-    load_b(c + 3, bq[(s_ + 3) % 4]);
+    if constexpr (b_req) load_b(c + 3, bq[(s_ + 3) % 4]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -322,16 +343,18 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
         mma_group(i, afr[cur], bq[s_]);
         mma_group(i, afr[cur + 1], bq[s_]);
         if (i + 1 < 8) read_a2(rs, i + 1, afr[nxt], afr[nxt + 1]);
-        else read_a2(rs1, 0, afr[nxt], afr[nxt + 1]);
+        else if constexpr (next_reads) read_a2(rs1, 0, afr[nxt], afr[nxt + 1]);
       } else {
         mma_group(i, afr[i % 4], bq[s_]);
         if (i + 2 < 8) read_a(rs, i + 2, afr[(i + 2) % 4]);
-        else read_a(rs1, i - 6, afr[(i + 2) % 4]);
+        else if constexpr (next_reads) read_a(rs1, i - 6, afr[(i + 2) % 4]);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (i == 5) {
-        form_w(w_r[wuse], wd_r[wuse], ws);
-        if constexpr (s_ == 3) __syncthreads();
+        if constexpr (sel) {
+          form_w(w_r[wuse], wd_r[wuse], ws);
+          if constexpr (s_ == 3) __syncthreads();
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -368,16 +391,34 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
   }
 
   static_assert(kBRing == 4, "the step is unrolled for a ring of 4");
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  auto group = [&](int c0, auto Ph) {
+    step(c0, S0{}, Ph);
+    step(c0 + 1, S1{}, Ph);
+    step(c0 + 2, S2{}, Ph);
+    step(c0 + 3, S3{}, Ph);
+  };
+  using All = std::integral_constant<int, kAll>;
   int c = 0;
-  for (; c + 4 <= nch; c += 4) {
-    step(c, std::integral_constant<int, 0>{});
-    step(c + 1, std::integral_constant<int, 1>{});
-    step(c + 2, std::integral_constant<int, 2>{});
-    step(c + 3, std::integral_constant<int, 3>{});
+  if constexpr (kPhased) {
+    // every request of a group starting at c is for a chunk below nch while c + 12 <= nch
+    for (; c + 12 <= nch; c += 4) group(c, All{});
+    group(c, std::integral_constant<int, kPenult>{});
+    group(c + 4, std::integral_constant<int, kLast>{});
+  } else {
+    for (; c + 4 <= nch; c += 4) {
+      step(c, S0{}, All{});
+      step(c + 1, S1{}, All{});
+      step(c + 2, S2{}, All{});
+      step(c + 3, S3{}, All{});
+    }
+    if (c < nch) step(c, S0{}, All{});
+    if (c + 1 < nch) step(c + 1, S1{}, All{});
+    if (c + 2 < nch) step(c + 2, S2{}, All{});
   }
-  if (c < nch) step(c, std::integral_constant<int, 0>{});
-  if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>{});
-  if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>{});
 
   // Cell state of this lane's 8 x 4 cells: tile-private, stored in accumulator order, so each
   // row group is one 16-byte access per lane and 1 KB per wave.
