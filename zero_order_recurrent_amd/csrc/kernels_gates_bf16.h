@@ -401,13 +401,35 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     step(c0 + 2, S2{}, Ph);
     step(c0 + 3, S3{}, Ph);
   };
+  // This lane's cell state: tile-private, stored in accumulator order, so each row group is one
+  // 16-byte access per lane and 1 KB per wave. It is read and written once per launch by this
+  // workgroup alone: its accesses (and the h stores) are marked non-temporal, which keeps them
+  // from displacing the weight and activation lines that the workgroups of an XCD share in L2
+  // (charlm launch -1.5 to -2.2%). The phased instance requests it early, into the activation
+  // registers its last steps no longer fill: row groups 0-3 into those of chunk nch - 4 before the
+  // second of the last four steps, 4-7 into those of chunk nch - 3 before the third (at the first
+  // timestep it reads whatever the buffer holds, in bounds, and uses zeros). A generic lambda, so
+  // that only the phased instance instantiates it.
+  auto c_early = [&](auto& dst, auto I0) {
+    constexpr int i0 = decltype(I0)::value;
+    const int64_t tile = (static_cast<int64_t>(pr) * a.n_col_blocks + cb) * a.n_row_tiles + rt;
+    const f32x4* cp = reinterpret_cast<const f32x4*>(a.c_tile) + (tile * 8 + wave) * 8 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(cp + 64 * (i0 + i)));
+  };
   using All = std::integral_constant<int, kAll>;
   int c = 0;
   if constexpr (kPhased) {
     // every request of a group starting at c is for a chunk below nch while c + 12 <= nch
     for (; c + 12 <= nch; c += 4) group(c, All{});
     group(c, std::integral_constant<int, kPenult>{});
-    group(c + 4, std::integral_constant<int, kLast>{});
+    using Last = std::integral_constant<int, kLast>;
+    step(c + 4, S0{}, Last{});
+    c_early(bq[0], std::integral_constant<int, 0>{});
+    step(c + 5, S1{}, Last{});
+    c_early(bq[1], std::integral_constant<int, 4>{});
+    step(c + 6, S2{}, Last{});
+    step(c + 7, S3{}, Last{});
   } else {
     for (; c + 4 <= nch; c += 4) {
       step(c, S0{}, All{});
@@ -420,17 +442,16 @@ __global__ __launch_bounds__(kGateThreads, 1) void k_lstm_gates_bf16(GateArgs a)
     if (c + 2 < nch) step(c + 2, S2{}, All{});
   }
 
-  // Cell state of this lane's 8 x 4 cells: tile-private, stored in accumulator order, so each
-  // row group is one 16-byte access per lane and 1 KB per wave.
   const int64_t tile = (static_cast<int64_t>(pr) * a.n_col_blocks + cb) * a.n_row_tiles + rt;
   float4* cptr = reinterpret_cast<float4*>(a.c_tile) + (tile * 8 + wave) * 8 * 64 + lane;
-  // The cell state is read and written once per launch by this workgroup alone: its accesses
-  // (and the h stores) are marked non-temporal, which keeps them from displacing the weight and
-  // activation lines that the workgroups of an XCD share in L2 (charlm launch -1.5 to -2.2%).
   f32x4 cst[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    cst[i] = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(cptr + 64 * i));
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (kPhased)
+      cst[i] = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_bit_cast(f32x4, bq[i >> 2][i & 3]);
+    else
+      cst[i] = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(cptr + 64 * i));
+  }
   // ---- fused LSTM cell; h leaves from registers as whole 64-byte column segments -------------
   // Lane (row r = lane / 16, column lane % 16 of each 16-column block j) holds unit 4 i + r of row
   // group i. The bf16 h of row groups 2k and 2k + 1 share a register (units 8k + r and 8k + 4 + r),
