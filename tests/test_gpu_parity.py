@@ -379,6 +379,30 @@ def test_xcd_grouped_tile_order(oracle, hidden, pairs):
     run.close()
 
 
+@pytest.mark.parametrize("layers,embed,hidden", [(2, 128, 128), (1, 128, 256), (2, 256, 256), (1, 1024, 1024),
+                                                 (1, 1056, 1056), (1, 128, 1088)])
+def test_k_loop_end_instances(oracle, layers, embed, hidden):
+    # The gate kernel's phased instance (no requests past the last K chunk, the cell state loaded
+    # early) serves reductions of 8-64 chunks that are a multiple of 4, the plain one all others.
+    # K chunks per launch at the first timestep / later ones: 128 x 128, both layers: 4 / 8;
+    # 128 x 256: 4 / 12; 256 x 256, both layers: 8 / 16; 1024 x 1024: 32 / 64; 1056 x 1056: 33 /
+    # 66; 128 x 1088: 4 / 38. So the phased instance runs with 0, 1 and several full groups before
+    # its last two, beside the plain one, which also serves 66 chunks and counts that are not a
+    # multiple of 4.
+    c = b.make_config(layers, 50, embed, hidden, 40, 3, 2, "bf16", 1e-3, 1e-3, 83)
+    say(f"[gpu] K-loop end instances, L={layers} E={embed} H={hidden}")
+    theta, tokens = _inputs(c, 14)
+    run = HipRun(c, theta, tokens)
+    losses, seq, st = run.probe_losses(0)
+    assert st == 0
+    probes, seqs = [0, 1], [0, 17, 39]
+    ref_l, ref_seq = oracle.probe_losses(ocfg(c), theta, tokens, 0, probe_ids=probes, seq_ids=seqs)
+    rows = [2 * i + s for i in probes for s in (0, 1)]
+    assert_losses_close(seq[np.ix_(rows, seqs)], ref_seq, 2e-2, "seq_losses")
+    assert_diffs_close(seq[np.ix_(rows, seqs)], ref_seq)
+    run.close()
+
+
 @pytest.mark.parametrize("name", list(PROBE_CASES))
 def test_probe_dominant_bf16(oracle, name):
     # eps = 2^-3 .. 2^-7 against weights of 1/sqrt(H) (or theta = 0): the probe moves the losses by
