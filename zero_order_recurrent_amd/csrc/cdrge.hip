@@ -252,6 +252,44 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 
 }  // namespace
 
+namespace {
+
+// k_update_perm instance for G = ceil(K / 8) groups of 8 probes (K <= 64)
+template <int kG>
+void launch_update_perm_g(dim3 grid, size_t lds, hipStream_t s, uint16_t* theta, const UpdTensors& ut,
+                          const uint64_t* seeds, const float* losses, int K, float coef, uint32_t* flags) {
+  hipLaunchKernelGGL(k_update_perm<kG>, grid, dim3(kUpdPermThreads), lds, s, theta, ut, seeds, losses, K, coef, flags);
+}
+
+void launch_update_perm(int G, dim3 grid, size_t lds, hipStream_t s, uint16_t* theta, const UpdTensors& ut,
+                        const uint64_t* seeds, const float* losses, int K, float coef, uint32_t* flags) {
+  switch (G) {
+    case 1: return launch_update_perm_g<1>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    case 2: return launch_update_perm_g<2>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    case 3: return launch_update_perm_g<3>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    case 4: return launch_update_perm_g<4>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    case 5: return launch_update_perm_g<5>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    case 6: return launch_update_perm_g<6>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    case 7: return launch_update_perm_g<7>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+    default: return launch_update_perm_g<8>(grid, lds, s, theta, ut, seeds, losses, K, coef, flags);
+  }
+}
+
+const void* update_perm_kernel(int G) {
+  switch (G) {
+    case 1: return reinterpret_cast<const void*>(k_update_perm<1>);
+    case 2: return reinterpret_cast<const void*>(k_update_perm<2>);
+    case 3: return reinterpret_cast<const void*>(k_update_perm<3>);
+    case 4: return reinterpret_cast<const void*>(k_update_perm<4>);
+    case 5: return reinterpret_cast<const void*>(k_update_perm<5>);
+    case 6: return reinterpret_cast<const void*>(k_update_perm<6>);
+    case 7: return reinterpret_cast<const void*>(k_update_perm<7>);
+    default: return reinterpret_cast<const void*>(k_update_perm<8>);
+  }
+}
+
+}  // namespace
+
 struct cdrge_ctx {
   Plan plan;
   void* params = nullptr;
@@ -728,8 +766,8 @@ cdrge_status enqueue_update(cdrge_ctx* ctx, uint64_t step, const float* losses) 
       const dim3 pgrid(static_cast<uint32_t>(need < ctx->n_cu ? need : ctx->n_cu));
       const size_t lds = update_perm_bytes(p.K);
       return timed(ctx, 2, bytes, [&] {
-        hipLaunchKernelGGL(k_update_perm, pgrid, dim3(kUpdPermThreads), lds, s,
-                           static_cast<uint16_t*>(th), ut, seeds, losses, p.K, coef, flags);
+        launch_update_perm((p.K + 7) / 8, pgrid, lds, s, static_cast<uint16_t*>(th), ut, seeds, losses, p.K, coef,
+                           flags);
       });
     }
     const int64_t blocks = (segs + kUpdLutThreads / 4 - 1) / (kUpdLutThreads / 4);
@@ -780,7 +818,7 @@ hipError_t set_update_lds(cdrge_ctx* ctx, bool bf16) {
   const int K = p.K;
   ctx->update_perm = false;
   if (update_perm_ok(p)) {
-    const void* f = reinterpret_cast<const void*>(k_update_perm);
+    const void* f = update_perm_kernel((ctx->plan.K + 7) / 8);
     hipFuncAttributes fa{};
     const hipError_t e = hipFuncGetAttributes(&fa, f);
     if (e != hipSuccess) return e;
