@@ -302,6 +302,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--copy-rate", action="store_true",
+                    help="only time plain device copies (torch's copy_) of 1 GiB and of an lstm1b theta "
+                         "(2.22 GB): the read + write rate an update kernel is compared with")
     ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--worker-probe", default="0", help=argparse.SUPPRESS)
     ap.add_argument("--worker-seqs", default="0", help=argparse.SUPPRESS)
@@ -318,6 +321,27 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_direction": n * 4, "copies": 3}), flush=True)
+        return
+    if args.copy_rate:
+        import torch
+        out = []
+        for nbytes in (1 << 30, 2 * 1110076466):
+            a = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+            b = torch.empty_like(a)
+            for _ in range(3):
+                b.copy_(a)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            e0.record()
+            for _ in range(reps):
+                b.copy_(a)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out.append({"bytes_per_direction": nbytes, "ms_per_copy": ms,
+                        "read_plus_write_gbs": 2 * nbytes / (ms / 1e3) / 1e9})
+            del a, b
+        print(json.dumps({"copy": "torch copy_ (bf16), HIP events on the current stream", "runs": out}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (sharding the probes across GPUs "
